@@ -1,0 +1,210 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) routed-expert layer library `libmoe.so`.
+ *
+ * The layer is the routed Mixture-of-Experts expert block of a Kimi-K3-style model on one
+ * GPU's local share of experts, forward and backward:
+ *   - routing: top-k of each token's router logits, softmax over the k kept values
+ *     ("Inside Kimi K3", section "Idea One", routing snippet);
+ *   - expert forward a_e = SiTU(W_gate x, W_up x), o_e = W_down a_e, y = sum_e p_e o_e and
+ *     the backward that takes dL/dp_e as <W_down^T dL/dy, a_e> so o_e is never stored
+ *     ("Kimi K3 ... Memory", section "MoE 反向", forward equation and p-gradient rewrite);
+ *   - SiTU-GLU: gate' = beta tanh(g/beta) sigmoid(g), lin' = linear_beta tanh(l/linear_beta),
+ *     a = gate' lin', gate half first; only the bf16 pre-activation [R, 2H] is kept and tanh
+ *     and sigmoid are recomputed in the backward ("Frontier-scale RL with Kimi K3", section
+ *     "Streaming activations");
+ *   - the backward redoes the dispatch from the pre-dispatch input ("MoE 反向", second saving).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers (hipMalloc'd or torch CUDA memory) unless a
+ *     comment says otherwise. The caller owns every buffer; the library never allocates.
+ *   - Layout is row-major and contiguous. bf16 tensors are passed as `void*` holding IEEE
+ *     bfloat16 bit patterns. Weights are [out, in]: w_gu[e] is [2H, d] with the H W_gate rows
+ *     first and the H W_up rows second; w_down[e] is [d, H].
+ *   - Every call is asynchronous on `stream` (0 = the null stream). Calls are thread-safe:
+ *     the library keeps no mutable global state besides a cached device-property table.
+ *   - Host-side validation runs before any launch; on error nothing is launched and the
+ *     output contents are unchanged. After MOE_ERR_HIP, moe_last_hip_error() gives the
+ *     hipError_t of the failed launch on the calling thread.
+ *   - Pointers to bf16/fp32 tensors must be 16-byte aligned; d and H must be multiples of
+ *     64; k <= 32; E <= 1024; E_loc <= 1024.
+ *   - Routed rows R are data-dependent and stay on the device in expert_offsets[E_loc].
+ *     Buffers indexed by rows are sized by a caller-chosen capacity R_cap (T*k always
+ *     suffices). moe_permute clamps the offsets to R_cap and raises *status_flag when the
+ *     true row count exceeds it, so the later calls never touch rows >= R_cap.
+ *   - y, dx and dp are this GPU's additive partial sums over its local experts (zero for
+ *     routes to other GPUs' experts), so summing them over GPUs gives the full layer.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,         /* a required pointer is NULL */
+  MOE_ERR_SHAPE = 2,        /* inconsistent or negative sizes (k > E, e_lo + E_loc > E, ...) */
+  MOE_ERR_UNSUPPORTED = 3,  /* outside the supported envelope (alignment, d/H % 64, k > 32) */
+  MOE_ERR_WORKSPACE = 4,    /* ws_bytes below moe_workspace_size() */
+  MOE_ERR_CAPACITY = 5,     /* reserved: the device-side row overflow is reported by flag */
+  MOE_ERR_HIP = 6           /* a HIP launch failed; see moe_last_hip_error() */
+} moe_status;
+
+/* Entry-point ids for moe_workspace_size(). */
+typedef enum {
+  MOE_WS_PERMUTE = 1,
+  MOE_WS_SITU_GLU_FWD = 2,
+  MOE_WS_SITU_GLU_BWD = 3,
+  MOE_WS_DOWN_COMBINE = 4,
+  MOE_WS_EXPERT_BWD = 5
+} moe_ws_kind;
+
+/* Static, NUL-terminated description of a status code. Never NULL. */
+const char* moe_status_string(moe_status s);
+
+/* hipError_t (as int) of the last MOE_ERR_HIP returned on this thread, 0 if none. */
+int moe_last_hip_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int moe_version(void);
+
+/*
+ * moe_route_topk - routing ("Inside Kimi K3", "Idea One"): for each token t, keep the k
+ * largest of logits[t, 0..E) and set gates[t, :] = softmax over those k values.
+ *   logits    [T, E] fp32, finite (precondition; not checked on the device).
+ *   topk_idx  [T, k] int32 out: global expert ids in slot order = value descending, equal
+ *             values by lower expert index (-0.0 ties +0.0).
+ *   gates     [T, k] fp32 out: exp(v_j - v_0) / sum_i exp(v_i - v_0), computed in fp32.
+ * Errors: NULL pointers (when T > 0), T < 0, E < 1, k < 1, k > E, k > 32, E > 1024.
+ */
+moe_status moe_route_topk(const float* logits, int64_t T, int E, int k,
+                          int32_t* topk_idx, float* gates, hipStream_t stream);
+
+/*
+ * moe_permute - dispatch metadata on one GPU ("MoE 反向", second saving: the grouped GEMM
+ * reads the tokens arranged by expert). Keeps routes to experts e_lo..e_lo+E_loc-1 and
+ * sorts them by local expert, stably by token within an expert (a counting sort; no atomic
+ * decides an order, so the result is bit-reproducible).
+ *   topk_idx, gates  [T, k] from moe_route_topk.
+ *   expert_offsets   [E_loc+1] int32 out: row range of local expert e is
+ *                    [offsets[e], offsets[e+1]); values clamped to R_cap.
+ *   row_token        [R_cap] int32 out: token of each row.
+ *   row_gate         [R_cap] fp32 out: gate of each row (not renormalised).
+ *   slot_row         [T, k] int32 out: row of route (t, j); -1 for non-local routes and for
+ *                    routes dropped because they fall beyond R_cap.
+ *   status_flag      device int32 out: 0, or 1 when the local route count exceeds R_cap.
+ *   ws, ws_bytes     device scratch of moe_workspace_size(MOE_WS_PERMUTE, ...) bytes.
+ * Errors: NULL pointers, e_lo < 0, E_loc < 1, E_loc > 1024, k > 32, R_cap < 0, small ws.
+ */
+moe_status moe_permute(const int32_t* topk_idx, const float* gates, int64_t T, int k,
+                       int e_lo, int E_loc, int64_t R_cap,
+                       int32_t* expert_offsets, int32_t* row_token, float* row_gate,
+                       int32_t* slot_row, int32_t* status_flag,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_unpermute - combine: out[t, :] = bf16( sum over j with slot_row[t,j] >= 0 of
+ * w(r) * rows[r, :] ), r = slot_row[t, j], w = row_weight[r] or 1 when row_weight is NULL;
+ * the sum is taken in fp32 in slot order. Tokens with no local route get zeros.
+ *   rows [R_cap, n] bf16, slot_row [T, k] int32, row_weight [R_cap] fp32 or NULL,
+ *   out [T, n] bf16. n must be a multiple of 8.
+ */
+moe_status moe_unpermute(const void* rows, const int32_t* slot_row, const float* row_weight,
+                         int64_t T, int k, int n, void* out, hipStream_t stream);
+
+/*
+ * moe_grouped_gemm_gate_up - for every local expert e and its rows r:
+ *   h[r, :]  = bf16( x[row_token[r], :] . w_gu[e]^T )           (saved for the backward)
+ *   a[r, j]  = bf16( SiTU-GLU(h[r, j], h[r, H + j]) ), j < H      (input of the down GEMM)
+ * The dispatch (row gather through row_token) is fused into the operand load; SiTU-GLU is
+ * fused into the epilogue and computed in fp32 from the bf16-rounded h.
+ *   x [T, d] bf16, row_token [R_cap], expert_offsets [E_loc+1] (device), w_gu
+ *   [E_loc, 2H, d] bf16, h [R_cap, 2H] bf16 out, a [R_cap, H] bf16 out.
+ */
+moe_status moe_grouped_gemm_gate_up(const void* x, const int32_t* row_token,
+                                    const int32_t* expert_offsets, int E_loc, int64_t R_cap,
+                                    int d, int H, const void* w_gu, float beta,
+                                    float linear_beta, void* h, void* a, hipStream_t stream);
+
+/*
+ * situ_glu_fwd - streaming SiTU-GLU: a[r, j] = bf16(gate'(h[r, j]) * lin'(h[r, H + j])).
+ *   h [R, 2H] bf16, a [R, H] bf16 out. fp32 math in registers; the kernel needs no memory
+ *   beyond its inputs and outputs, so `ws` may be NULL and moe_workspace_size reports 0
+ *   (the constant-size fp32 working set is the per-wave register tile, independent of R).
+ * H must be a multiple of 8.
+ */
+moe_status situ_glu_fwd(const void* h, int64_t R, int H, float beta, float linear_beta,
+                        void* a, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * situ_glu_bwd - dh = [da * lin' * dgate'/dg , da * gate' * dlin'/dl] with tanh and sigmoid
+ * recomputed from h ("Streaming activations", custom op item 1).
+ *   h [R, 2H] bf16, da [R, H] bf16, dh [R, 2H] bf16 out (may not alias h or da).
+ */
+moe_status situ_glu_bwd(const void* h, const void* da, int64_t R, int H, float beta,
+                        float linear_beta, void* dh, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/*
+ * moe_grouped_gemm_down_combine - o[r, :] = a[r, :] . w_down[e]^T for the rows of each
+ * local expert, then y[t, :] = bf16( sum_j p_j o[slot_row[t, j], :] ) ("MoE 反向", forward
+ * equation). o is a transient of this call (bf16(p o) rows in `ws`), never kept.
+ *   a [R_cap, H] bf16, row_gate [R_cap] fp32, slot_row [T, k], w_down [E_loc, d, H] bf16,
+ *   y [T, d] bf16 out, ws of moe_workspace_size(MOE_WS_DOWN_COMBINE, ...) bytes.
+ */
+moe_status moe_grouped_gemm_down_combine(const void* a, const int32_t* expert_offsets,
+                                         const float* row_gate, const int32_t* slot_row,
+                                         int64_t T, int k, int E_loc, int64_t R_cap, int H,
+                                         int d, const void* w_down, void* y,
+                                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_expert_bwd - backward of the expert layer with dL/dy = dy ("MoE 反向"):
+ *   G      = dy[row_token] . w_down[e]                        (re-dispatch of dy fused)
+ *   a      = SiTU-GLU(h) recomputed exactly as in the forward epilogue
+ *   dp     = <G, a> per row        (dL/dp_e = <W_down^T dL/dy, a_e>; o_e is never used)
+ *   dh     = SiTU-GLU'(h) applied to da = p G                 (bf16, transient in ws)
+ *   dw_down[e] = sum_r (p_r dy_r) a_r^T                        fp32, overwritten
+ *   dw_gu[e]   = sum_r dh_r x_r^T                              fp32, overwritten
+ *   dx[t]  = bf16( sum_j (dh . w_gu[e])[slot_row[t, j]] )
+ *   dp[t, j] = dp of row slot_row[t, j], 0 for non-local slots.
+ * Experts with no rows get dw = 0.
+ *   dy, x [T, d] bf16; h [R_cap, 2H] bf16 (saved by the forward); metadata from
+ *   moe_permute; dx [T, d] bf16 out; dw_gu [E_loc, 2H, d] fp32 out; dw_down [E_loc, d, H]
+ *   fp32 out; dp [T, k] fp32 out; ws of moe_workspace_size(MOE_WS_EXPERT_BWD, ...) bytes.
+ */
+moe_status moe_expert_bwd(const void* dy, const void* x, const void* h,
+                          const int32_t* row_token, const float* row_gate,
+                          const int32_t* slot_row, const int32_t* expert_offsets,
+                          int64_t T, int k, int E_loc, int64_t R_cap, int d, int H,
+                          const void* w_gu, const void* w_down, float beta, float linear_beta,
+                          void* dx, float* dw_gu, float* dw_down, float* dp,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * moe_router_bwd - gradient through the softmax over the kept logits: with p the gates and
+ * g = dL/dp, dlogit_kept[t, j] = p_j (g_j - sum_i p_i g_i) (fp32). Logits that were not kept
+ * do not reach the output. Only meaningful when all k routes of a token are local (or dp
+ * has been summed over GPUs).
+ *   gates, dp [T, k] fp32; dlogits_kept [T, k] fp32 out.
+ */
+moe_status moe_router_bwd(const float* gates, const float* dp, int64_t T, int k,
+                          float* dlogits_kept, hipStream_t stream);
+
+/*
+ * moe_workspace_size - bytes of `ws` the entry point `which` needs for these sizes
+ * (arguments that do not apply are ignored). Host-only; launches nothing.
+ */
+moe_status moe_workspace_size(int which, int64_t T, int E_loc, int k, int d, int H,
+                              int64_t R_cap, size_t* bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,275 @@
+"""ctypes binding of libmoe.so: one Python function per C entry point, same names.
+
+Argument marshalling only: tensors are checked for device, dtype and contiguity and passed
+as raw device pointers together with torch's current HIP stream; outputs that the caller
+does not pass are allocated with torch (memory plumbing). Every step of the computation runs
+in the library's HIP kernels. There is no CPU fallback: if libmoe.so is missing or fails to
+load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "moe.h")
+
+MOE_WS_PERMUTE, MOE_WS_SITU_GLU_FWD, MOE_WS_SITU_GLU_BWD, MOE_WS_DOWN_COMBINE, MOE_WS_EXPERT_BWD = 1, 2, 3, 4, 5
+
+_lock = threading.Lock()
+_lib = None
+
+
+class MoEError(RuntimeError):
+    """A libmoe.so call returned a non-OK status."""
+
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: status {status}: {msg}")
+        self.status = status
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I = ctypes.c_int
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+_SIGS = {
+    "moe_status_string": (ctypes.c_char_p, [_I]),
+    "moe_last_hip_error": (_I, []),
+    "moe_version": (_I, []),
+    "moe_route_topk": (_I, [_P, _I64, _I, _I, _P, _P, _P]),
+    "moe_permute": (_I, [_P, _P, _I64, _I, _I, _I, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_unpermute": (_I, [_P, _P, _P, _I64, _I, _I, _P, _P]),
+    "moe_grouped_gemm_gate_up": (_I, [_P, _P, _P, _I, _I64, _I, _I, _P, _F, _F, _P, _P, _P]),
+    "situ_glu_fwd": (_I, [_P, _I64, _I, _F, _F, _P, _P, _SZ, _P]),
+    "situ_glu_bwd": (_I, [_P, _P, _I64, _I, _F, _F, _P, _P, _SZ, _P]),
+    "moe_grouped_gemm_down_combine": (_I, [_P, _P, _P, _P, _I64, _I, _I, _I64, _I, _I, _P, _P,
+                                           _P, _SZ, _P]),
+    "moe_expert_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I64, _I, _I, _I64, _I, _I, _P, _P, _F,
+                            _F, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_router_bwd": (_I, [_P, _P, _I64, _I, _P, _P]),
+    "moe_workspace_size": (_I, [_I, _I64, _I, _I, _I, _I, _I64, ctypes.POINTER(_SZ)]),
+}
+
+
+def header_functions(path: str = HEADER_PATH) -> list:
+    """Names of the functions include/moe.h declares (parsed from the header text)."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+
+
+def load():
+    """Load libmoe.so once (raises OSError with a clear message when it is not built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise OSError(f"{LIB_PATH} is not built; run sparse_moe_expert_top_amd.build.build()")
+            lib = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in _SIGS.items():
+                f = getattr(lib, name)
+                f.restype = res
+                f.argtypes = args
+            _lib = lib
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        lib = load()
+        msg = lib.moe_status_string(status).decode()
+        if status == 6:
+            msg += f" (hipError {lib.moe_last_hip_error()})"
+        raise MoEError(fn, status, msg)
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def workspace_size(which: int, T=0, E_loc=1, k=1, d=64, H=64, R_cap=0) -> int:
+    out = _SZ(0)
+    _check("moe_workspace_size", load().moe_workspace_size(which, T, E_loc, k, d, H, R_cap,
+                                                           ctypes.byref(out)))
+    return int(out.value)
+
+
+def _ws(nbytes, device):
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# --------------------------------------------------------------------------- entry points
+def moe_route_topk(logits, k, topk_idx=None, gates=None, stream=None):
+    T, E = logits.shape
+    _need(logits, "logits", torch.float32)
+    dev = logits.device
+    topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev) if topk_idx is None else topk_idx
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev) if gates is None else gates
+    _need(topk_idx, "topk_idx", torch.int32, (T, k))
+    _need(gates, "gates", torch.float32, (T, k))
+    _check("moe_route_topk", load().moe_route_topk(_ptr(logits), T, E, k, _ptr(topk_idx),
+                                                   _ptr(gates), _stream(stream)))
+    return topk_idx, gates
+
+
+def moe_permute(topk_idx, gates, e_lo, E_loc, R_cap, out=None, ws=None, stream=None):
+    """Returns dict(offsets, row_token, row_gate, slot_row, status)."""
+    T, k = topk_idx.shape
+    _need(topk_idx, "topk_idx", torch.int32)
+    _need(gates, "gates", torch.float32, (T, k))
+    dev = topk_idx.device
+    if out is None:
+        out = dict(offsets=torch.empty(E_loc + 1, dtype=torch.int32, device=dev),
+                   row_token=torch.empty(max(R_cap, 1), dtype=torch.int32, device=dev),
+                   row_gate=torch.empty(max(R_cap, 1), dtype=torch.float32, device=dev),
+                   slot_row=torch.empty((T, k), dtype=torch.int32, device=dev),
+                   status=torch.empty(1, dtype=torch.int32, device=dev))
+    need = workspace_size(MOE_WS_PERMUTE, T=T, E_loc=E_loc)
+    ws = _ws(need, dev) if ws is None else ws
+    _check("moe_permute", load().moe_permute(
+        _ptr(topk_idx), _ptr(gates), T, k, e_lo, E_loc, R_cap, _ptr(out["offsets"]),
+        _ptr(out["row_token"]), _ptr(out["row_gate"]), _ptr(out["slot_row"]), _ptr(out["status"]),
+        _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+def moe_unpermute(rows, slot_row, row_weight=None, out=None, stream=None):
+    T, k = slot_row.shape
+    n = rows.shape[1]
+    _need(rows, "rows", torch.bfloat16)
+    _need(slot_row, "slot_row", torch.int32)
+    if row_weight is not None:
+        _need(row_weight, "row_weight", torch.float32)
+    out = torch.empty((T, n), dtype=torch.bfloat16, device=rows.device) if out is None else out
+    _need(out, "out", torch.bfloat16, (T, n))
+    _check("moe_unpermute", load().moe_unpermute(_ptr(rows), _ptr(slot_row), _ptr(row_weight), T,
+                                                 k, n, _ptr(out), _stream(stream)))
+    return out
+
+
+def moe_grouped_gemm_gate_up(x, row_token, offsets, w_gu, R_cap, beta=4.0, linear_beta=25.0,
+                             h=None, a=None, stream=None):
+    E_loc, H2, d = w_gu.shape
+    H = H2 // 2
+    _need(x, "x", torch.bfloat16)
+    _need(w_gu, "w_gu", torch.bfloat16)
+    _need(row_token, "row_token", torch.int32)
+    _need(offsets, "offsets", torch.int32, (E_loc + 1,))
+    dev = x.device
+    h = torch.empty((R_cap, 2 * H), dtype=torch.bfloat16, device=dev) if h is None else h
+    a = torch.empty((R_cap, H), dtype=torch.bfloat16, device=dev) if a is None else a
+    _need(h, "h", torch.bfloat16)
+    _need(a, "a", torch.bfloat16)
+    _check("moe_grouped_gemm_gate_up", load().moe_grouped_gemm_gate_up(
+        _ptr(x), _ptr(row_token), _ptr(offsets), E_loc, R_cap, d, H, _ptr(w_gu), beta,
+        linear_beta, _ptr(h), _ptr(a), _stream(stream)))
+    return h, a
+
+
+def situ_glu_fwd(h, beta=4.0, linear_beta=25.0, a=None, stream=None):
+    R, H2 = h.shape
+    H = H2 // 2
+    _need(h, "h", torch.bfloat16)
+    a = torch.empty((R, H), dtype=torch.bfloat16, device=h.device) if a is None else a
+    _need(a, "a", torch.bfloat16, (R, H))
+    _check("situ_glu_fwd", load().situ_glu_fwd(_ptr(h), R, H, beta, linear_beta, _ptr(a), None,
+                                               0, _stream(stream)))
+    return a
+
+
+def situ_glu_bwd(h, da, beta=4.0, linear_beta=25.0, dh=None, stream=None):
+    R, H2 = h.shape
+    H = H2 // 2
+    _need(h, "h", torch.bfloat16)
+    _need(da, "da", torch.bfloat16, (R, H))
+    dh = torch.empty_like(h) if dh is None else dh
+    _need(dh, "dh", torch.bfloat16, (R, 2 * H))
+    _check("situ_glu_bwd", load().situ_glu_bwd(_ptr(h), _ptr(da), R, H, beta, linear_beta,
+                                               _ptr(dh), None, 0, _stream(stream)))
+    return dh
+
+
+def moe_grouped_gemm_down_combine(a, offsets, row_gate, slot_row, w_down, R_cap, y=None,
+                                  ws=None, stream=None):
+    E_loc, d, H = w_down.shape
+    T, k = slot_row.shape
+    _need(a, "a", torch.bfloat16)
+    _need(w_down, "w_down", torch.bfloat16)
+    _need(row_gate, "row_gate", torch.float32)
+    _need(slot_row, "slot_row", torch.int32)
+    dev = a.device
+    y = torch.empty((T, d), dtype=torch.bfloat16, device=dev) if y is None else y
+    _need(y, "y", torch.bfloat16, (T, d))
+    need = workspace_size(MOE_WS_DOWN_COMBINE, T=T, E_loc=E_loc, k=k, d=d, H=H, R_cap=R_cap)
+    ws = _ws(need, dev) if ws is None else ws
+    _check("moe_grouped_gemm_down_combine", load().moe_grouped_gemm_down_combine(
+        _ptr(a), _ptr(offsets), _ptr(row_gate), _ptr(slot_row), T, k, E_loc, R_cap, H, d,
+        _ptr(w_down), _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def moe_expert_bwd(dy, x, h, perm, w_gu, w_down, R_cap, beta=4.0, linear_beta=25.0,
+                   dx=None, dw_gu=None, dw_down=None, dp=None, ws=None, stream=None):
+    """perm: dict with offsets, row_token, row_gate, slot_row (from moe_permute)."""
+    E_loc, H2, d = w_gu.shape
+    H = H2 // 2
+    T, k = perm["slot_row"].shape
+    _need(dy, "dy", torch.bfloat16, (T, d))
+    _need(x, "x", torch.bfloat16, (T, d))
+    _need(h, "h", torch.bfloat16)
+    _need(w_gu, "w_gu", torch.bfloat16)
+    _need(w_down, "w_down", torch.bfloat16, (E_loc, d, H))
+    dev = dy.device
+    dx = torch.empty((T, d), dtype=torch.bfloat16, device=dev) if dx is None else dx
+    dw_gu = torch.empty((E_loc, 2 * H, d), dtype=torch.float32, device=dev) if dw_gu is None else dw_gu
+    dw_down = torch.empty((E_loc, d, H), dtype=torch.float32, device=dev) if dw_down is None else dw_down
+    dp = torch.empty((T, k), dtype=torch.float32, device=dev) if dp is None else dp
+    _need(dx, "dx", torch.bfloat16, (T, d))
+    _need(dw_gu, "dw_gu", torch.float32, (E_loc, 2 * H, d))
+    _need(dw_down, "dw_down", torch.float32, (E_loc, d, H))
+    _need(dp, "dp", torch.float32, (T, k))
+    need = workspace_size(MOE_WS_EXPERT_BWD, T=T, E_loc=E_loc, k=k, d=d, H=H, R_cap=R_cap)
+    ws = _ws(need, dev) if ws is None else ws
+    _check("moe_expert_bwd", load().moe_expert_bwd(
+        _ptr(dy), _ptr(x), _ptr(h), _ptr(perm["row_token"]), _ptr(perm["row_gate"]),
+        _ptr(perm["slot_row"]), _ptr(perm["offsets"]), T, k, E_loc, R_cap, d, H, _ptr(w_gu),
+        _ptr(w_down), beta, linear_beta, _ptr(dx), _ptr(dw_gu), _ptr(dw_down), _ptr(dp),
+        _ptr(ws), ws.numel(), _stream(stream)))
+    return dx, dw_gu, dw_down, dp
+
+
+def moe_router_bwd(gates, dp, out=None, stream=None):
+    T, k = gates.shape
+    _need(gates, "gates", torch.float32)
+    _need(dp, "dp", torch.float32, (T, k))
+    out = torch.empty_like(gates) if out is None else out
+    _check("moe_router_bwd", load().moe_router_bwd(_ptr(gates), _ptr(dp), T, k, _ptr(out),
+                                                   _stream(stream)))
+    return out

@@ -1,0 +1,547 @@
+// Grouped bf16 GEMMs of the routed-expert layer on gfx950 MFMA, with fused epilogues.
+//
+// "Kimi K3 ... Memory", section "MoE 反向": each expert computes a_e = SiTU(W_gate x, W_up x),
+// o_e = W_down a_e, y = sum p_e o_e; the backward gets dL/dp_e = <W_down^T dL/dy, a_e> and
+// dL/da_e = p_e W_down^T dL/dy, redoing the dispatch from the pre-dispatch input. The six
+// contractions below are that layer; every one runs over all local experts in one launch:
+//
+//   name      C[m][n]                         M        N     K       A kind       B kind
+//   gate_up   x[tok(r)] . w_gu[e]^T           rows     2H    d       rows+gather  rows (NT)
+//   down      a[r] . w_down[e]^T              rows     d     H       rows         rows (NT)
+//   dA        dy[tok(r)] . w_down[e]          rows     H     d       rows+gather  k-outer (NN)
+//   dX        dh[r] . w_gu[e]                 rows     d     2H      rows         k-outer (NN)
+//   dW_down   sum_r dy[tok(r)]^T pa[r]        d        H     rows    k-outer+g    k-outer (TN)
+//   dW_gu     sum_r dh[r]^T x[tok(r)]         2H       d     rows    k-outer      k-outer+g
+//
+// Design (gfx950):
+//  * v_mfma_f32_32x32x16_bf16, fp32 accumulators; 4 wavefronts per workgroup in a 2x2 grid,
+//    each owning a (BM/2) x (BN/2) block of C.
+//  * Operands are staged through LDS as [row][64 k] bf16 tiles (two stages, one barrier per
+//    k-step). The 16-byte chunk c of row r sits at chunk position c ^ ((r ^ r>>3) & 7), so
+//    the MFMA fragment reads (8 consecutive rows, same chunk) and the transposing stores
+//    (rows 8 apart, same chunk) both hit distinct banks.
+//  * "rows" operands are K-contiguous in HBM and load 16 bytes per lane, optionally through a
+//    row index (the dispatch gather). "k-outer" operands are stored with K as the outer
+//    index; each lane loads a (BM/32)-row x 8-column block and transposes it in registers
+//    (byte permutes) before the LDS store, so every MFMA reads K-contiguous fragments.
+//  * Ragged extents come from the device-side expert offsets: a persistent grid walks a tile
+//    list built in LDS from those offsets (no host sync). Consecutive tile ids go to the
+//    same XCD (workgroup i runs on XCD i mod 8), so the m-tiles sharing one expert's weight
+//    panel run together and share that XCD's L2.
+//  * Epilogues: gate_up writes h (bf16) and a = bf16(SiTU-GLU(bf16 h)); down writes
+//    bf16(p * o) rows for the combine; dA recomputes a from the saved h, accumulates the
+//    per-row <G, a> partials, and writes dh and bf16(p a); dX writes bf16 rows; the weight
+//    gradients write fp32 (zeros for experts without rows).
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "launch.h"
+#include "situ_math.h"
+
+namespace moe {
+
+constexpr int kBK = 64;              // bf16 elements of K per LDS stage
+constexpr int kThreads = 256;
+
+enum BKind { B_ROWS = 0, B_KOUT = 1 };
+enum Epi { EPI_GATEUP = 0, EPI_ROWS_SCALED = 1, EPI_ROWS = 2, EPI_DA = 3, EPI_F32 = 4 };
+
+struct GemmArgs {
+  const uint16_t* A;
+  int64_t lda;
+  const int32_t* a_gather;
+  const uint16_t* B;
+  int64_t ldb;
+  int64_t b_gstride;
+  const int32_t* b_gather;
+  const int32_t* offsets;
+  int G;
+  int M, N, K;       // fixed extents; the ragged one comes from offsets
+  int H;             // split of the gate/linear halves (gate_up, dA)
+  int n_tiles;       // tiles along N (gate_up: along the H gate/linear column pairs)
+  int m_tiles;       // tiles along M (weight gradients)
+  uint16_t* o0;
+  int64_t ld0;
+  uint16_t* o1;
+  int64_t ld1;
+  float* of;
+  int64_t ldf;
+  int64_t f_gstride;
+  const float* row_scale;
+  const uint16_t* hsrc;
+  float* dp_part;
+  int64_t dp_ld;
+  SituCoef sc;
+};
+
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  return row * kBK + ((chunk ^ swz(row)) << 3);
+}
+
+// Column c (0..7) of a pair of 8-wide rows, as one dword {x[c], y[c]}.
+__device__ __forceinline__ uint32_t pair_col(const u32x4& x, const u32x4& y, int c) {
+  const uint32_t a = x[c >> 1], b = y[c >> 1];
+  return (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+}
+
+// Store a k-outer register block (KB rows of 8 columns, rows k0..k0+KB-1 of the stage,
+// columns col0..col0+7 of the tile) transposed into the [col][k] LDS tile.
+template <int KB>
+__device__ __forceinline__ void store_kout(uint16_t* lds, const u32x4 (&reg)[KB], int col0,
+                                           int k0) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const int row = col0 + c;
+    if constexpr (KB == 8) {
+      u32x4 w;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) w[p] = pair_col(reg[2 * p], reg[2 * p + 1], c);
+      *(u32x4*)&lds[lds_off(row, k0 >> 3)] = w;
+    } else if constexpr (KB == 4) {
+      u32x2 w;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) w[p] = pair_col(reg[2 * p], reg[2 * p + 1], c);
+      *(u32x2*)&lds[lds_off(row, k0 >> 3) + (k0 & 7)] = w;
+    } else {
+      static_assert(KB == 2, "k-outer block height");
+      *(uint32_t*)&lds[lds_off(row, k0 >> 3) + (k0 & 7)] = pair_col(reg[0], reg[1], 0 + c);
+    }
+  }
+}
+
+template <int BM, int BN, bool KRAG, int BKIND, int EPI>
+__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(GemmArgs p) {
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int FM = WM / 32, FN = WN / 32;
+  constexpr int NA = BM / 32;        // 16-byte registers per lane for an A stage
+  constexpr int NB = BN / 32;        // ... for a B stage
+  static_assert(!KRAG || BKIND == B_KOUT, "weight gradients read B k-outer");
+  static_assert(EPI != EPI_GATEUP || (FN % 2 == 0), "gate/linear pairs");
+
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * kBK];
+  __shared__ int s_pref[1025];
+  __shared__ int s_scan[kThreads];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ---------------------------------------------------------------- tile list
+  int total;
+  if constexpr (KRAG) {
+    total = p.G * p.m_tiles * p.n_tiles;
+  } else {
+    int loc[4];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int g = tid * 4 + i;
+      int c = 0;
+      if (g < p.G) {
+        const int mg = p.offsets[g + 1] - p.offsets[g];
+        c = ((mg + BM - 1) / BM) * p.n_tiles;
+      }
+      loc[i] = c;
+      sum += c;
+    }
+    s_scan[tid] = sum;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+      const int v = (tid >= off) ? s_scan[tid - off] : 0;
+      __syncthreads();
+      s_scan[tid] += v;
+      __syncthreads();
+    }
+    int run = s_scan[tid] - sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int g = tid * 4 + i;
+      if (g < p.G) s_pref[g] = run;
+      run += loc[i];
+    }
+    total = s_scan[kThreads - 1];
+    if (tid == 0) s_pref[p.G] = total;
+    __syncthreads();
+  }
+
+  const int nblk = gridDim.x;
+  const int b = blockIdx.x;
+  const int first = ((nblk & 7) == 0) ? ((b & 7) * (nblk >> 3) + (b >> 3)) : b;
+
+  for (int tile = first; tile < total; tile += nblk) {
+    int g, mt, nt;
+    if constexpr (KRAG) {
+      const int per = p.m_tiles * p.n_tiles;
+      g = tile / per;
+      const int rem = tile - g * per;
+      nt = rem / p.m_tiles;
+      mt = rem - nt * p.m_tiles;
+    } else {
+      int lo = 0, hi = p.G;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_pref[mid] <= tile) lo = mid; else hi = mid;
+      }
+      g = lo;
+      const int mg = p.offsets[g + 1] - p.offsets[g];
+      const int mtg = (mg + BM - 1) / BM;
+      const int local = tile - s_pref[g];
+      nt = local / mtg;
+      mt = local - nt * mtg;
+    }
+    const int r0 = p.offsets[g];
+    const int gcount = p.offsets[g + 1] - r0;
+    const int Mg = KRAG ? p.M : gcount;
+    const int Kg = KRAG ? gcount : p.K;
+    const int nk = (Kg + kBK - 1) / kBK;
+    const int m0 = mt * BM;
+    const int n0 = nt * BN;
+    const int j0 = nt * (BN / 2);          // gate_up: first gate/linear column pair
+
+    // ------------------------------------------------------------ operand addressing
+    const uint16_t* a_ptr[NA];
+    int a_col = 0;
+    if constexpr (!KRAG) {
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        const int rr = (tid >> 3) + 32 * i;
+        const int m = min(m0 + rr, Mg - 1);
+        const int srow = p.a_gather ? p.a_gather[r0 + m] : (r0 + m);
+        a_ptr[i] = p.A + (int64_t)srow * p.lda + (tid & 7) * 8;
+      }
+    } else {
+      a_col = min(m0 + (tid % (BM / 8)) * 8, p.M - 8);
+    }
+    const uint16_t* b_ptr[NB];
+    int b_col = 0;
+    const uint16_t* Bg = p.B + (int64_t)g * p.b_gstride;
+    if constexpr (BKIND == B_ROWS) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int nn = (tid >> 3) + 32 * i;
+        int wrow;
+        if constexpr (EPI == EPI_GATEUP) {
+          const int w = nn / WN, q = nn % WN;
+          const int jj = min(j0 + w * (WN / 2) + (q % (WN / 2)), p.H - 1);
+          wrow = (q < WN / 2) ? jj : p.H + jj;
+        } else {
+          wrow = min(n0 + nn, p.N - 1);
+        }
+        b_ptr[i] = Bg + (int64_t)wrow * p.ldb + (tid & 7) * 8;
+      }
+    } else {
+      b_col = min(n0 + (tid % (BN / 8)) * 8, p.N - 8);
+    }
+    const int a_kb = tid / (BM / 8);       // k-outer block index (rows a_kb*NA ..)
+    const int b_kb = tid / (BN / 8);
+
+    u32x4 ra[NA], rb[NB];
+    auto load_stage = [&](int kt) {
+      const int kbase = kt * kBK;
+      if constexpr (!KRAG) {
+#pragma unroll
+        for (int i = 0; i < NA; ++i) ra[i] = *(const u32x4*)(a_ptr[i] + kbase);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < NA; ++kk) {
+          const int kg = kbase + a_kb * NA + kk;
+          if (kg < Kg) {
+            const int srow = p.a_gather ? p.a_gather[r0 + kg] : (r0 + kg);
+            ra[kk] = *(const u32x4*)(p.A + (int64_t)srow * p.lda + a_col);
+          } else {
+            ra[kk] = u32x4{0u, 0u, 0u, 0u};
+          }
+        }
+      }
+      if constexpr (BKIND == B_ROWS) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i) rb[i] = *(const u32x4*)(b_ptr[i] + kbase);
+      } else if constexpr (!KRAG) {
+#pragma unroll
+        for (int kk = 0; kk < NB; ++kk)
+          rb[kk] = *(const u32x4*)(Bg + (int64_t)(kbase + b_kb * NB + kk) * p.ldb + b_col);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < NB; ++kk) {
+          const int kg = kbase + b_kb * NB + kk;
+          if (kg < Kg) {
+            const int srow = p.b_gather ? p.b_gather[r0 + kg] : (r0 + kg);
+            rb[kk] = *(const u32x4*)(p.B + (int64_t)srow * p.ldb + b_col);
+          } else {
+            rb[kk] = u32x4{0u, 0u, 0u, 0u};
+          }
+        }
+      }
+    };
+    auto store_stage = [&](int buf) {
+      if constexpr (!KRAG) {
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+          *(u32x4*)&sA[buf][lds_off((tid >> 3) + 32 * i, tid & 7)] = ra[i];
+      } else {
+        store_kout<NA>(sA[buf], ra, (tid % (BM / 8)) * 8, a_kb * NA);
+      }
+      if constexpr (BKIND == B_ROWS) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+          *(u32x4*)&sB[buf][lds_off((tid >> 3) + 32 * i, tid & 7)] = rb[i];
+      } else {
+        store_kout<NB>(sB[buf], rb, (tid % (BN / 8)) * 8, b_kb * NB);
+      }
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    auto compute_stage = [&](int buf) {
+#pragma unroll
+      for (int s = 0; s < kBK / 16; ++s) {
+        const int ch = 2 * s + (lane >> 5);
+        bf16x8 af[FM], bfr[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          af[i] = *(const bf16x8*)&sA[buf][lds_off(wm * WM + i * 32 + (lane & 31), ch)];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          bfr[j] = *(const bf16x8*)&sB[buf][lds_off(wn * WN + j * 32 + (lane & 31), ch)];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
+    };
+
+    if (nk > 0) {
+      load_stage(0);
+      store_stage(0);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + 1 < nk) load_stage(kt + 1);
+      compute_stage(kt & 1);
+      if (kt + 1 < nk) store_stage((kt + 1) & 1);
+      __syncthreads();
+    }
+
+    // ------------------------------------------------------------ epilogues
+    // acc[i][j][v] holds C[row][col] with row = i*32 + 8*(v/4) + 4*(lane/32) + v%4 and
+    // col = j*32 + lane%32 inside the wavefront's block.
+    const int col_l = lane & 31;
+    const int rq = (lane >> 5) * 4;
+    if constexpr (EPI == EPI_F32) {
+      float* Cg = p.of + (int64_t)g * p.f_gstride;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = n0 + wn * WN + j * 32 + col_l;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = m0 + wm * WM + i * 32 + (v >> 2) * 8 + rq + (v & 3);
+            if (row < p.M && col < p.N) Cg[(int64_t)row * p.ldf + col] = acc[i][j][v];
+          }
+        }
+    } else if constexpr (EPI == EPI_ROWS || EPI == EPI_ROWS_SCALED) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = m0 + wm * WM + i * 32 + (v >> 2) * 8 + rq + (v & 3);
+          if (row >= Mg) continue;
+          const int64_t r = r0 + row;
+          float sc = 1.0f;
+          if constexpr (EPI == EPI_ROWS_SCALED) sc = p.row_scale[r];
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int col = n0 + wn * WN + j * 32 + col_l;
+            if (col < p.N) p.o0[r * p.ld0 + col] = f32_to_bf16(acc[i][j][v] * sc);
+          }
+        }
+    } else if constexpr (EPI == EPI_GATEUP) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = m0 + wm * WM + i * 32 + (v >> 2) * 8 + rq + (v & 3);
+          if (row >= Mg) continue;
+          const int64_t r = r0 + row;
+#pragma unroll
+          for (int j = 0; j < FN / 2; ++j) {
+            const int jj = j0 + wn * (WN / 2) + j * 32 + col_l;
+            if (jj >= p.H) continue;
+            const uint16_t hg = f32_to_bf16(acc[i][j][v]);
+            const uint16_t hl = f32_to_bf16(acc[i][j + FN / 2][v]);
+            p.o0[r * p.ld0 + jj] = hg;
+            p.o0[r * p.ld0 + p.H + jj] = hl;
+            p.o1[r * p.ld1 + jj] = f32_to_bf16(situ_fwd(bf16_to_f32(hg), bf16_to_f32(hl), p.sc));
+          }
+        }
+    } else if constexpr (EPI == EPI_DA) {
+      const int slot = nt * 2 + wn;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = m0 + wm * WM + i * 32 + (v >> 2) * 8 + rq + (v & 3);
+          const bool vr = row < Mg;
+          const int64_t r = r0 + (vr ? row : 0);
+          const float pr = vr ? p.row_scale[r] : 0.0f;
+          float part = 0.0f;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int n = n0 + wn * WN + j * 32 + col_l;
+            if (vr && n < p.N) {
+              const float gv = acc[i][j][v];
+              const uint16_t* hr = p.hsrc + r * (2 * (int64_t)p.H);
+              float a, dgv, dlv;
+              situ_bwd(bf16_to_f32(hr[n]), bf16_to_f32(hr[p.H + n]), pr * gv, p.sc, a, dgv, dlv);
+              const float ab = round_bf16(a);
+              part += gv * ab;
+              uint16_t* dr = p.o0 + r * p.ld0;
+              dr[n] = f32_to_bf16(dgv);
+              dr[p.H + n] = f32_to_bf16(dlv);
+              p.o1[r * p.ld1 + n] = f32_to_bf16(pr * ab);
+            }
+          }
+          // sum over the 32 lanes that share this row
+#pragma unroll
+          for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+          if (vr && col_l == 0) p.dp_part[(int64_t)slot * p.dp_ld + r] = part;
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------- launchers
+template <int BM, int BN, bool KRAG, int BKIND, int EPI>
+static hipError_t run_gemm(const GemmArgs& args, int64_t max_tiles, hipStream_t s) {
+  auto kern = grouped_gemm_kernel<BM, BN, KRAG, BKIND, EPI>;
+  static int occ = -1;                   // workgroups per CU for this instantiation
+  if (occ < 0) {
+    int o = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, kThreads, 0) != hipSuccess || o < 1)
+      o = 1;
+    occ = o;
+  }
+  int64_t grid = (int64_t)device_cu_count() * occ;
+  if (max_tiles < grid) grid = max_tiles;
+  if (grid < 1) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, s, args);
+  return hipGetLastError();
+}
+
+constexpr int kTM = 128, kTN = 128;
+
+static GemmArgs blank_args() {
+  GemmArgs a;
+  __builtin_memset(&a, 0, sizeof(a));
+  return a;
+}
+
+static int64_t mragged_tile_bound(int64_t R_cap, int E_loc, int bm, int n_tiles) {
+  return ((R_cap + bm - 1) / bm + E_loc) * (int64_t)n_tiles;
+}
+
+hipError_t launch_gemm_gate_up(const uint16_t* x, const int32_t* row_token,
+                               const int32_t* offsets, int E_loc, int64_t R_cap, int d, int H,
+                               const uint16_t* w_gu, SituCoef c, uint16_t* h, uint16_t* a,
+                               hipStream_t s) {
+  GemmArgs p = blank_args();
+  p.A = x; p.lda = d; p.a_gather = row_token;
+  p.B = w_gu; p.ldb = d; p.b_gstride = (int64_t)2 * H * d;
+  p.offsets = offsets; p.G = E_loc;
+  p.N = 2 * H; p.K = d; p.H = H;
+  p.n_tiles = (H + kTN / 2 - 1) / (kTN / 2);
+  p.o0 = h; p.ld0 = 2 * H; p.o1 = a; p.ld1 = H;
+  p.sc = c;
+  return run_gemm<kTM, kTN, false, B_ROWS, EPI_GATEUP>(
+      p, mragged_tile_bound(R_cap, E_loc, kTM, p.n_tiles), s);
+}
+
+hipError_t launch_gemm_down(const uint16_t* a, const int32_t* offsets, const float* row_gate,
+                            int E_loc, int64_t R_cap, int H, int d, const uint16_t* w_down,
+                            uint16_t* rows_out, hipStream_t s) {
+  GemmArgs p = blank_args();
+  p.A = a; p.lda = H;
+  p.B = w_down; p.ldb = H; p.b_gstride = (int64_t)d * H;
+  p.offsets = offsets; p.G = E_loc;
+  p.N = d; p.K = H;
+  p.n_tiles = (d + kTN - 1) / kTN;
+  p.o0 = rows_out; p.ld0 = d; p.row_scale = row_gate;
+  return run_gemm<kTM, kTN, false, B_ROWS, EPI_ROWS_SCALED>(
+      p, mragged_tile_bound(R_cap, E_loc, kTM, p.n_tiles), s);
+}
+
+int gemm_da_slots(int H) { return ((H + kTN - 1) / kTN) * 2; }
+
+hipError_t launch_gemm_da(const uint16_t* dy, const int32_t* row_token, const int32_t* offsets,
+                          int E_loc, int64_t R_cap, int d, int H, const uint16_t* w_down,
+                          const uint16_t* h, const float* row_gate, SituCoef c, uint16_t* dh,
+                          uint16_t* pa, float* dp_part, hipStream_t s) {
+  GemmArgs p = blank_args();
+  p.A = dy; p.lda = d; p.a_gather = row_token;
+  p.B = w_down; p.ldb = H; p.b_gstride = (int64_t)d * H;      // B(n=j, k) = w_down[e][k][j]
+  p.offsets = offsets; p.G = E_loc;
+  p.N = H; p.K = d; p.H = H;
+  p.n_tiles = (H + kTN - 1) / kTN;
+  p.o0 = dh; p.ld0 = 2 * H; p.o1 = pa; p.ld1 = H;
+  p.row_scale = row_gate; p.hsrc = h; p.dp_part = dp_part; p.dp_ld = R_cap;
+  p.sc = c;
+  return run_gemm<kTM, kTN, false, B_KOUT, EPI_DA>(
+      p, mragged_tile_bound(R_cap, E_loc, kTM, p.n_tiles), s);
+}
+
+hipError_t launch_gemm_dx(const uint16_t* dh, const int32_t* offsets, int E_loc,
+                          int64_t R_cap, int d, int H, const uint16_t* w_gu,
+                          uint16_t* rows_out, hipStream_t s) {
+  GemmArgs p = blank_args();
+  p.A = dh; p.lda = 2 * H;
+  p.B = w_gu; p.ldb = d; p.b_gstride = (int64_t)2 * H * d;    // B(n, k) = w_gu[e][k][n]
+  p.offsets = offsets; p.G = E_loc;
+  p.N = d; p.K = 2 * H;
+  p.n_tiles = (d + kTN - 1) / kTN;
+  p.o0 = rows_out; p.ld0 = d;
+  return run_gemm<kTM, kTN, false, B_KOUT, EPI_ROWS>(
+      p, mragged_tile_bound(R_cap, E_loc, kTM, p.n_tiles), s);
+}
+
+hipError_t launch_gemm_dw_down(const uint16_t* dy, const int32_t* row_token,
+                               const uint16_t* pa, const int32_t* offsets, int E_loc, int d,
+                               int H, float* dw_down, hipStream_t s) {
+  GemmArgs p = blank_args();
+  p.A = dy; p.lda = d; p.a_gather = row_token;                // A(m, k=r) = dy[tok(r)][m]
+  p.B = pa; p.ldb = H;                                        // B(n, k=r) = pa[r][n]
+  p.offsets = offsets; p.G = E_loc;
+  p.M = d; p.N = H;
+  p.m_tiles = (d + kTM - 1) / kTM;
+  p.n_tiles = (H + kTN - 1) / kTN;
+  p.of = dw_down; p.ldf = H; p.f_gstride = (int64_t)d * H;
+  return run_gemm<kTM, kTN, true, B_KOUT, EPI_F32>(
+      p, (int64_t)E_loc * p.m_tiles * p.n_tiles, s);
+}
+
+hipError_t launch_gemm_dw_gu(const uint16_t* dh, const uint16_t* x, const int32_t* row_token,
+                             const int32_t* offsets, int E_loc, int d, int H, float* dw_gu,
+                             hipStream_t s) {
+  GemmArgs p = blank_args();
+  p.A = dh; p.lda = 2 * H;                                    // A(m, k=r) = dh[r][m]
+  p.B = x; p.ldb = d; p.b_gather = row_token;                 // B(n, k=r) = x[tok(r)][n]
+  p.offsets = offsets; p.G = E_loc;
+  p.M = 2 * H; p.N = d;
+  p.m_tiles = (2 * H + kTM - 1) / kTM;
+  p.n_tiles = (d + kTN - 1) / kTN;
+  p.of = dw_gu; p.ldf = d; p.f_gstride = (int64_t)2 * H * d;
+  return run_gemm<kTM, kTN, true, B_KOUT, EPI_F32>(
+      p, (int64_t)E_loc * p.m_tiles * p.n_tiles, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,65 @@
+// Internal launchers behind the C ABI (declared here, defined next to their kernels).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "situ_math.h"
+
+namespace moe {
+
+// Device facts used to size persistent grids (cached per device).
+int device_cu_count();
+
+// Routing and dispatch metadata ("Inside Kimi K3", "Idea One"; "MoE 反向", second saving).
+hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int32_t* idx,
+                             float* gates, hipStream_t s);
+int permute_blocks(int64_t T);
+size_t permute_ws_bytes(int64_t T, int E_loc);
+hipError_t launch_permute(const int32_t* idx, const float* gates, int64_t T, int k, int e_lo,
+                          int E_loc, int64_t R_cap, int32_t* offsets, int32_t* row_token,
+                          float* row_gate, int32_t* slot_row, int32_t* status, void* ws,
+                          hipStream_t s);
+hipError_t launch_unpermute(const uint16_t* rows, const int32_t* slot_row, const float* w,
+                            int64_t T, int k, int n, uint16_t* out, hipStream_t s);
+hipError_t launch_dp_reduce_scatter(float* part, int nslots, int64_t R_cap,
+                                    const int32_t* offsets, int E_loc,
+                                    const int32_t* slot_row, int64_t T, int k, float* dp,
+                                    hipStream_t s);
+hipError_t launch_router_bwd(const float* gates, const float* dp, int64_t T, int k,
+                             float* dlogits, hipStream_t s);
+
+// Streaming SiTU-GLU ("Frontier-scale RL with Kimi K3", "Streaming activations").
+hipError_t launch_situ_fwd(const uint16_t* h, int64_t R, int H, SituCoef c, uint16_t* a,
+                           hipStream_t s);
+hipError_t launch_situ_bwd(const uint16_t* h, const uint16_t* da, int64_t R, int H,
+                           SituCoef c, uint16_t* dh, hipStream_t s);
+
+// Grouped GEMMs ("MoE 反向": expert forward equation and the rewritten backward).
+// Rows of group e are [offsets[e], offsets[e+1]).
+hipError_t launch_gemm_gate_up(const uint16_t* x, const int32_t* row_token,
+                               const int32_t* offsets, int E_loc, int64_t R_cap, int d, int H,
+                               const uint16_t* w_gu, SituCoef c, uint16_t* h, uint16_t* a,
+                               hipStream_t s);
+hipError_t launch_gemm_down(const uint16_t* a, const int32_t* offsets, const float* row_gate,
+                            int E_loc, int64_t R_cap, int H, int d, const uint16_t* w_down,
+                            uint16_t* rows_out, hipStream_t s);
+// dA: G = dy[row_token] . w_down[e]; epilogue writes dh, pa = bf16(p a) and dp partials.
+int gemm_da_slots(int H);
+hipError_t launch_gemm_da(const uint16_t* dy, const int32_t* row_token, const int32_t* offsets,
+                          int E_loc, int64_t R_cap, int d, int H, const uint16_t* w_down,
+                          const uint16_t* h, const float* row_gate, SituCoef c, uint16_t* dh,
+                          uint16_t* pa, float* dp_part, hipStream_t s);
+// dX rows: dh . w_gu[e]  ->  bf16 rows [R, d]
+hipError_t launch_gemm_dx(const uint16_t* dh, const int32_t* offsets, int E_loc,
+                          int64_t R_cap, int d, int H, const uint16_t* w_gu,
+                          uint16_t* rows_out, hipStream_t s);
+// Weight gradients with ragged K = rows of the expert.
+hipError_t launch_gemm_dw_down(const uint16_t* dy, const int32_t* row_token,
+                               const uint16_t* pa, const int32_t* offsets, int E_loc, int d,
+                               int H, float* dw_down, hipStream_t s);
+hipError_t launch_gemm_dw_gu(const uint16_t* dh, const uint16_t* x, const int32_t* row_token,
+                             const int32_t* offsets, int E_loc, int d, int H, float* dw_gu,
+                             hipStream_t s);
+
+}  // namespace moe

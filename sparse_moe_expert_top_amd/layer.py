@@ -1,0 +1,101 @@
+"""The routed-expert layer (forward + backward) as a sequence of libmoe.so calls.
+
+Forward ("Kimi K3 ... Memory", section "MoE 反向", forward equation; routing as in "Inside
+Kimi K3", "Idea One"):
+    moe_route_topk -> moe_permute -> moe_grouped_gemm_gate_up -> moe_grouped_gemm_down_combine
+Saved for the backward: the pre-dispatch input x, the bf16 pre-activation h [R, 2H] and the
+routing metadata; a and o are not kept ("Frontier-scale RL with Kimi K3", "Streaming
+activations": only the bf16 input of the activation is saved).
+Backward: moe_expert_bwd (re-dispatch, dA + SiTU-GLU' + dp, dW_down, dW_gu, dX, combine).
+
+`LayerBuffers` allocates every buffer once (torch, HBM) so a training step issues only the
+library's kernels; buffers indexed by routed rows are sized by a capacity R_cap (T*k by
+default, which never overflows).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+
+
+@dataclass
+class LayerShape:
+    T: int
+    E: int
+    k: int
+    e_lo: int
+    E_loc: int
+    d: int
+    H: int
+    beta: float = 4.0
+    linear_beta: float = 25.0
+
+
+class LayerBuffers:
+    """Device buffers for one layer call of a given shape, reused across steps."""
+
+    def __init__(self, shape: LayerShape, R_cap: int | None = None, device="cuda"):
+        s = shape
+        self.shape = s
+        self.R_cap = s.T * s.k if R_cap is None else int(R_cap)
+        R = max(self.R_cap, 1)
+        i32, f32, bf = torch.int32, torch.float32, torch.bfloat16
+        e = lambda *sh, dt: torch.empty(sh, dtype=dt, device=device)
+        self.topk_idx = e(s.T, s.k, dt=i32)
+        self.gates = e(s.T, s.k, dt=f32)
+        self.perm = dict(offsets=e(s.E_loc + 1, dt=i32), row_token=e(R, dt=i32),
+                         row_gate=e(R, dt=f32), slot_row=e(s.T, s.k, dt=i32),
+                         status=e(1, dt=i32))
+        self.ws_perm = e(max(_lib.workspace_size(_lib.MOE_WS_PERMUTE, T=s.T, E_loc=s.E_loc), 256), dt=torch.uint8)
+        self.h = e(R, 2 * s.H, dt=bf)
+        self.a = e(R, s.H, dt=bf)
+        self.y = e(s.T, s.d, dt=bf)
+        self.ws_down = e(max(_lib.workspace_size(_lib.MOE_WS_DOWN_COMBINE, T=s.T, E_loc=s.E_loc,
+                                                 k=s.k, d=s.d, H=s.H, R_cap=self.R_cap), 256),
+                         dt=torch.uint8)
+        self.dx = e(s.T, s.d, dt=bf)
+        self.dw_gu = e(s.E_loc, 2 * s.H, s.d, dt=f32)
+        self.dw_down = e(s.E_loc, s.d, s.H, dt=f32)
+        self.dp = e(s.T, s.k, dt=f32)
+        self.ws_bwd = e(max(_lib.workspace_size(_lib.MOE_WS_EXPERT_BWD, T=s.T, E_loc=s.E_loc,
+                                                k=s.k, d=s.d, H=s.H, R_cap=self.R_cap), 256),
+                        dt=torch.uint8)
+
+    # ------------------------------------------------------------------ steps
+    def route(self, logits):
+        s = self.shape
+        _lib.moe_route_topk(logits, s.k, self.topk_idx, self.gates)
+        _lib.moe_permute(self.topk_idx, self.gates, s.e_lo, s.E_loc, self.R_cap, out=self.perm,
+                         ws=self.ws_perm)
+
+    def forward(self, x, logits, w_gu, w_down):
+        s = self.shape
+        self.route(logits)
+        _lib.moe_grouped_gemm_gate_up(x, self.perm["row_token"], self.perm["offsets"], w_gu,
+                                      self.R_cap, s.beta, s.linear_beta, h=self.h, a=self.a)
+        _lib.moe_grouped_gemm_down_combine(self.a, self.perm["offsets"], self.perm["row_gate"],
+                                           self.perm["slot_row"], w_down, self.R_cap, y=self.y,
+                                           ws=self.ws_down)
+        return self.y
+
+    def backward(self, dy, x, w_gu, w_down):
+        s = self.shape
+        _lib.moe_expert_bwd(dy, x, self.h, self.perm, w_gu, w_down, self.R_cap, s.beta,
+                            s.linear_beta, dx=self.dx, dw_gu=self.dw_gu, dw_down=self.dw_down,
+                            dp=self.dp, ws=self.ws_bwd)
+        return self.dx, self.dw_gu, self.dw_down, self.dp
+
+    def step(self, x, logits, w_gu, w_down, dy):
+        """One forward + backward pass of the layer."""
+        self.forward(x, logits, w_gu, w_down)
+        return self.backward(dy, x, w_gu, w_down)
+
+    def rows(self) -> int:
+        """Routed local rows R (reads 4 bytes back from the device: synchronises)."""
+        return int(self.perm["offsets"][-1].item())
+
+    def overflowed(self) -> bool:
+        return bool(self.perm["status"].item())

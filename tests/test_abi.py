@@ -1,0 +1,109 @@
+"""The C ABI library loads, exports every declared entry point, and rejects bad arguments on
+the host before any launch (these calls never reach the GPU, so they run on CPU)."""
+import ctypes
+
+import pytest
+
+import sparse_moe_expert_top_amd as moe
+from sparse_moe_expert_top_amd import _lib
+
+OK, ENULL, ESHAPE, EUNSUP, EWS = 0, 1, 2, 3, 4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return moe.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = moe.header_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib._SIGS, f"binding lacks {n}"
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert lib.moe_status_string(s)
+    assert lib.moe_status_string(99) == b"unknown status"
+    assert lib.moe_version() >= 100
+    assert lib.moe_last_hip_error() == 0
+
+
+def _ws(which, **kw):
+    out = ctypes.c_size_t(0)
+    args = dict(T=0, E_loc=1, k=1, d=64, H=64, R_cap=0)
+    args.update(kw)
+    st = moe.load().moe_workspace_size(which, args["T"], args["E_loc"], args["k"], args["d"],
+                                       args["H"], args["R_cap"], ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_sizes():
+    assert _ws(_lib.MOE_WS_SITU_GLU_FWD, T=10) == (OK, 0)
+    assert _ws(_lib.MOE_WS_SITU_GLU_BWD, T=10) == (OK, 0)
+    st, b = _ws(_lib.MOE_WS_PERMUTE, T=1000, E_loc=28)
+    assert st == OK and b >= 28 * 4 * 4 and b % 256 == 0
+    st, b = _ws(_lib.MOE_WS_DOWN_COMBINE, d=3584, H=3072, R_cap=1000)
+    assert st == OK and b >= 1000 * 3584 * 2
+    st, b = _ws(_lib.MOE_WS_EXPERT_BWD, d=3584, H=3072, R_cap=1000)
+    assert st == OK and b >= 1000 * 6144 * 2 + 1000 * 3584 * 2
+    assert _ws(_lib.MOE_WS_EXPERT_BWD, d=100, H=3072, R_cap=10)[0] == EUNSUP
+    assert _ws(_lib.MOE_WS_PERMUTE, E_loc=0)[0] == ESHAPE
+    assert _ws(77)[0] == ESHAPE
+    assert moe.load().moe_workspace_size(1, 0, 1, 1, 64, 64, 0, None) == ENULL
+
+
+def test_route_rejects(lib):
+    P = ctypes.c_void_p(16)
+    assert lib.moe_route_topk(P, -1, 8, 2, P, P, None) == ESHAPE
+    assert lib.moe_route_topk(P, 4, 8, 9, P, P, None) == ESHAPE       # k > E
+    assert lib.moe_route_topk(P, 4, 8, 0, P, P, None) == ESHAPE
+    assert lib.moe_route_topk(P, 4, 2000, 2, P, P, None) == EUNSUP    # E > 1024
+    assert lib.moe_route_topk(P, 4, 64, 33, P, P, None) == EUNSUP     # k > 32
+    assert lib.moe_route_topk(None, 4, 8, 2, P, P, None) == ENULL
+    assert lib.moe_route_topk(None, 0, 8, 2, None, None, None) == OK  # empty: nothing to do
+
+
+def test_permute_rejects(lib):
+    P = ctypes.c_void_p(256)
+    args = [P, P, 16, 2, 0, 4, 32, P, P, P, P, P, P, 1 << 20, None]
+    assert lib.moe_permute(*args[:5], 0, *args[6:]) == ESHAPE          # E_loc = 0
+    a = list(args); a[4] = -1
+    assert lib.moe_permute(*a) == ESHAPE
+    a = list(args); a[13] = 0
+    assert lib.moe_permute(*a) == EWS
+    a = list(args); a[11] = None
+    assert lib.moe_permute(*a) == ENULL                                # status flag
+    a = list(args); a[3] = 40
+    assert lib.moe_permute(*a) == EUNSUP                               # k > 32
+
+
+def test_gemm_and_situ_reject(lib):
+    P = ctypes.c_void_p(256)
+    U = ctypes.c_void_p(258)                                           # not 16-byte aligned
+    assert lib.moe_grouped_gemm_gate_up(P, P, P, 4, 100, 100, 64, P, 4.0, 25.0, P, P, None) == EUNSUP
+    assert lib.moe_grouped_gemm_gate_up(P, P, P, 4, 100, 128, 64, P, 4.0, 25.0, U, P, None) == EUNSUP
+    assert lib.moe_grouped_gemm_gate_up(P, P, None, 4, 100, 128, 64, P, 4.0, 25.0, P, P, None) == ENULL
+    assert lib.moe_grouped_gemm_gate_up(P, P, P, 4, 100, 128, 64, P, -1.0, 25.0, P, P, None) == ESHAPE
+    assert lib.situ_glu_fwd(P, 10, 12, 4.0, 25.0, P, None, 0, None) == EUNSUP     # H % 8
+    assert lib.situ_glu_fwd(None, 10, 16, 4.0, 25.0, P, None, 0, None) == ENULL
+    assert lib.situ_glu_bwd(P, P, -5, 16, 4.0, 25.0, P, None, 0, None) == ESHAPE
+    assert lib.situ_glu_fwd(None, 0, 16, 4.0, 25.0, None, None, 0, None) == OK
+    assert lib.moe_unpermute(P, P, None, 4, 2, 12, P, None) == EUNSUP             # n % 8
+    assert lib.moe_grouped_gemm_down_combine(P, P, P, P, 8, 2, 4, 16, 64, 128, P, P, P, 0, None) == EWS
+    assert lib.moe_router_bwd(None, P, 4, 2, P, None) == ENULL
+
+
+def test_expert_bwd_rejects(lib):
+    P = ctypes.c_void_p(256)
+    base = [P, P, P, P, P, P, P, 8, 2, 4, 16, 128, 64, P, P, 4.0, 25.0, P, P, P, P, P, 1 << 30, None]
+    a = list(base); a[22] = 10
+    assert lib.moe_expert_bwd(*a) == EWS
+    a = list(base); a[11] = 96
+    assert lib.moe_expert_bwd(*a) == EUNSUP
+    a = list(base); a[13] = None
+    assert lib.moe_expert_bwd(*a) == ENULL
+    a = list(base); a[8] = 0
+    assert lib.moe_expert_bwd(*a) == ESHAPE

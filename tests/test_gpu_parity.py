@@ -1,0 +1,387 @@
+"""GPU parity: every libmoe.so entry point against the fp64 oracle (mode S).
+
+Bars: integer outputs (indices, offsets, rows, slots) bit-exact; bf16 outputs and the fp32
+weight gradients max|gpu - oracle| / max|oracle| <= 1e-2; fp32 gates and dp <= 2e-3.
+Small shapes are compared in full; the full-size workloads (one expert-parallel rank,
+skewed routing, large context) run in the benchmark's launch configuration and are compared
+on sampled tokens, rows and weight-gradient columns, plus properties that hold at any size.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_inputs import LAYER_CONFIGS, LayerConfig, SITU_CONFIGS, layer_inputs, situ_inputs
+from tests._helpers import rel_err, BF16_TOL, FP32_TOL, sub_perm, oracle_route_perm
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def moe():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm GPU")
+    import sparse_moe_expert_top_amd as m
+    m.load()
+    return m
+
+
+def dev_bf16(u16):
+    return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def host_bf16(t):
+    return oracle.bf16_widen(t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16))
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def run_layer(m, cfg, inp, R_cap=None):
+    """Forward + backward through LayerBuffers (the benchmark's launch configuration)."""
+    shape = m.LayerShape(T=inp["x"].shape[0], E=cfg.E, k=cfg.k, e_lo=cfg.e_lo, E_loc=cfg.E_loc,
+                         d=cfg.d, H=cfg.H, beta=cfg.beta, linear_beta=cfg.linear_beta)
+    buf = m.LayerBuffers(shape, R_cap=R_cap)
+    t = dict(x=dev_bf16(inp["x"]), logits=dev(inp["logits"]), w_gu=dev_bf16(inp["w_gu"]),
+             w_down=dev_bf16(inp["w_down"]), dy=dev_bf16(inp["dy"]))
+    buf.step(t["x"], t["logits"], t["w_gu"], t["w_down"], t["dy"])
+    torch.cuda.synchronize()
+    return buf, t
+
+
+def check_route_perm(buf, idx, gates, perm, R_cap=None):
+    assert np.array_equal(buf.topk_idx.cpu().numpy(), idx)
+    assert rel_err(buf.gates.cpu().numpy(), gates) <= FP32_TOL
+    R = perm["R"]
+    off = buf.perm["offsets"].cpu().numpy()
+    assert np.array_equal(off, perm["offsets"])
+    assert np.array_equal(buf.perm["row_token"][:R].cpu().numpy(), perm["row_token"])
+    assert np.array_equal(buf.perm["slot_row"].cpu().numpy(), perm["slot_row"])
+    # row_gate is the GPU's own gate of that route, bit for bit
+    g_gpu = buf.gates.cpu().numpy()
+    sr = perm["slot_row"]
+    t, j = np.nonzero(sr >= 0)
+    assert np.array_equal(buf.perm["row_gate"][:R].cpu().numpy()[sr[t, j]], g_gpu[t, j])
+    assert int(buf.perm["status"].item()) == 0
+
+
+# ------------------------------------------------------------------------------- SiTU-GLU
+@pytest.mark.parametrize("R,H", [(1000, 192), (37, 64), (1, 8)])
+def test_situ_glu_small(moe, R, H):
+    say(f"situ_glu R={R} H={H}")
+    inp = situ_inputs(R, H, seed=3)
+    h = dev_bf16(inp["h"])
+    da = dev_bf16(inp["da"])
+    a = moe.situ_glu_fwd(h)
+    dh = moe.situ_glu_bwd(h, da)
+    torch.cuda.synchronize()
+    hf = oracle.bf16_widen(inp["h"])
+    ref_a = oracle.bf16_round(oracle.situ_glu_fwd(hf, H))
+    ref_dh = oracle.bf16_round(oracle.situ_glu_bwd(hf, oracle.bf16_widen(inp["da"]), H))
+    assert rel_err(host_bf16(a), ref_a) <= BF16_TOL
+    assert rel_err(host_bf16(dh), ref_dh) <= BF16_TOL
+
+
+def test_situ_glu_extremes(moe):
+    """Saturated and special inputs stay finite and match the oracle's limits."""
+    H = 8
+    g = np.array([0.0, -0.0, 1e-30, -1e-30, 88.0, -88.0, 200.0, -200.0, 3e38, -3e38, 0.5, -1.2188,
+                  4.0, -4.0, 30.0, -30.0], np.float32)
+    l = np.array([0.0, 1.0, -1.0, 1e4, -1e4, 3e38, -3e38, 25.0, 0.5, -0.5, 100.0, 2.0, -60.0,
+                  60.0, 1e-20, 7.0], np.float32)
+    from moe_inputs import f32_to_bf16_bits
+    hb = f32_to_bf16_bits(np.concatenate([g.reshape(2, 8), l.reshape(2, 8)], axis=1))
+    da = f32_to_bf16_bits(np.ones((2, 8), np.float32))
+    a = moe.situ_glu_fwd(dev_bf16(hb))
+    dh = moe.situ_glu_bwd(dev_bf16(hb), dev_bf16(da))
+    torch.cuda.synchronize()
+    ga, gdh = host_bf16(a), host_bf16(dh)
+    assert np.all(np.isfinite(ga)) and np.all(np.isfinite(gdh))
+    hf = oracle.bf16_widen(hb)
+    ref_a = oracle.bf16_round(oracle.situ_glu_fwd(hf, H))
+    ref_dh = oracle.bf16_round(oracle.situ_glu_bwd(hf, oracle.bf16_widen(da), H))
+    np.testing.assert_allclose(ga, ref_a, rtol=1e-2, atol=1e-35)   # fp32 denormals may flush
+    np.testing.assert_allclose(gdh, ref_dh, rtol=1e-2, atol=1e-6)
+
+
+def test_situ_glu_full_size_sampled(moe):
+    """h bf16 [131072, 6144] ~ N(0, 9), da [131072, 3072]: the streaming configuration; the
+    oracle checks 4096 sampled rows."""
+    cfg = SITU_CONFIGS["situ"]
+    R, H = cfg["R"], cfg["H"]
+    say(f"situ_glu full R={R} H={H}")
+    inp = situ_inputs(R, H, seed=0, h_std=cfg["h_std"])
+    h = dev_bf16(inp["h"])
+    da = dev_bf16(inp["da"])
+    a = moe.situ_glu_fwd(h)
+    dh = moe.situ_glu_bwd(h, da)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(0).choice(R, 4096, replace=False))
+    rows = np.concatenate([rows, [0, R - 1]])
+    hf = oracle.bf16_widen(inp["h"][rows])
+    ref_a = oracle.bf16_round(oracle.situ_glu_fwd(hf, H))
+    ref_dh = oracle.bf16_round(oracle.situ_glu_bwd(hf, oracle.bf16_widen(inp["da"][rows]), H))
+    ridx = torch.from_numpy(rows).cuda()
+    assert rel_err(host_bf16(a[ridx]), ref_a) <= BF16_TOL
+    assert rel_err(host_bf16(dh[ridx]), ref_dh) <= BF16_TOL
+    assert bool(torch.isfinite(a.float()).all()) and bool(torch.isfinite(dh.float()).all())
+
+
+# ------------------------------------------------------------------------------- routing
+@pytest.mark.parametrize("name", ["tiny", "shard", "skew", "large"])
+def test_route_and_permute(moe, name):
+    cfg = LAYER_CONFIGS[name]
+    say(f"route/permute {name}")
+    rng = np.random.default_rng(0)
+    logits = rng.standard_normal((cfg.T, cfg.E), dtype=np.float32)
+    if cfg.bias:
+        from moe_inputs import zipf_bias
+        logits += zipf_bias(cfg.E)[None, :]
+    idx, gates = oracle.route_topk(logits, cfg.k)
+    g_idx, g_gates = moe.moe_route_topk(dev(logits), cfg.k)
+    assert np.array_equal(g_idx.cpu().numpy(), idx)
+    assert rel_err(g_gates.cpu().numpy(), gates) <= FP32_TOL
+    assert float((g_gates.sum(1) - 1).abs().max()) <= 1e-5
+    perm = oracle.permute(idx, gates, cfg.e_lo, cfg.E_loc)
+    R_cap = cfg.T * cfg.k
+    out = moe.moe_permute(g_idx, g_gates, cfg.e_lo, cfg.E_loc, R_cap)
+    torch.cuda.synchronize()
+    assert np.array_equal(out["offsets"].cpu().numpy(), perm["offsets"])
+    assert np.array_equal(out["row_token"][:perm["R"]].cpu().numpy(), perm["row_token"])
+    assert np.array_equal(out["slot_row"].cpu().numpy(), perm["slot_row"])
+    assert int(out["status"].item()) == 0
+
+
+def test_route_ties(moe):
+    """Equal logits (and -0.0 vs +0.0) resolve to the lower expert index."""
+    rng = np.random.default_rng(5)
+    L = rng.integers(-2, 3, size=(513, 130)).astype(np.float32)
+    L[0] = 0.0
+    L[1, ::2] = -0.0
+    for k in (1, 7, 32):
+        idx, gates = oracle.route_topk(L, k)
+        g_idx, g_gates = moe.moe_route_topk(dev(L), k)
+        assert np.array_equal(g_idx.cpu().numpy(), idx)
+        assert rel_err(g_gates.cpu().numpy(), gates) <= FP32_TOL
+
+
+def test_permute_capacity_overflow(moe):
+    """R_cap below the routed rows: flag raised, offsets clamped, dropped routes get -1."""
+    cfg = LAYER_CONFIGS["tiny"]
+    rng = np.random.default_rng(1)
+    logits = rng.standard_normal((cfg.T, cfg.E), dtype=np.float32)
+    idx, gates = oracle.route_topk(logits, cfg.k)
+    perm = oracle.permute(idx, gates, 0, cfg.E_loc)
+    R_cap = perm["R"] - 100
+    g_idx, g_gates = moe.moe_route_topk(dev(logits), cfg.k)
+    out = moe.moe_permute(g_idx, g_gates, 0, cfg.E_loc, R_cap)
+    torch.cuda.synchronize()
+    assert int(out["status"].item()) == 1
+    assert np.array_equal(out["offsets"].cpu().numpy(), np.minimum(perm["offsets"], R_cap))
+    sr = out["slot_row"].cpu().numpy()
+    ref = np.where(perm["slot_row"] < R_cap, perm["slot_row"], -1)
+    assert np.array_equal(sr, ref)
+    assert np.array_equal(out["row_token"][:R_cap].cpu().numpy(), perm["row_token"][:R_cap])
+
+
+def test_unpermute(moe):
+    rng = np.random.default_rng(2)
+    from moe_inputs import f32_to_bf16_bits
+    rows = f32_to_bf16_bits(rng.standard_normal((300, 64)).astype(np.float32))
+    slot_row = rng.integers(-1, 300, size=(50, 5)).astype(np.int32)
+    w = rng.random(300).astype(np.float32)
+    out = moe.moe_unpermute(dev_bf16(rows), dev(slot_row), dev(w))
+    out_nw = moe.moe_unpermute(dev_bf16(rows), dev(slot_row))
+    torch.cuda.synchronize()
+    ref = oracle.bf16_round(oracle.unpermute_sum(rows, slot_row, w.astype(np.float64)))
+    assert rel_err(host_bf16(out), ref) <= BF16_TOL
+    ref = oracle.bf16_round(oracle.unpermute_sum(rows, slot_row))
+    assert rel_err(host_bf16(out_nw), ref) <= BF16_TOL
+
+
+def test_router_bwd(moe):
+    rng = np.random.default_rng(3)
+    logits = rng.standard_normal((100, 20)).astype(np.float32)
+    idx, gates = oracle.route_topk(logits, 6)
+    dp = rng.standard_normal((100, 6)).astype(np.float32)
+    g_idx, g_gates = moe.moe_route_topk(dev(logits), 6)
+    out = moe.moe_router_bwd(g_gates, dev(dp))
+    torch.cuda.synchronize()
+    assert rel_err(out.cpu().numpy(), oracle.router_bwd(gates, dp)) <= FP32_TOL
+
+
+# ------------------------------------------------------------------------------- layer, full compare
+MID = LayerConfig("mid", T=2048, d=256, H=192, E=16, k=4, e_lo=2, E_loc=10)
+SMALL_CASES = {
+    "tiny": LAYER_CONFIGS["tiny"],
+    "mid": MID,                                                           # several tiles + ragged tails
+    "one_token": LayerConfig("one_token", T=1, d=128, H=64, E=8, k=3, e_lo=0, E_loc=8),
+    "k_eq_E": LayerConfig("k_eq_E", T=64, d=64, H=128, E=6, k=6, e_lo=0, E_loc=6),
+    "none_local": LayerConfig("none_local", T=128, d=128, H=64, E=64, k=2, e_lo=60, E_loc=4),
+    "skew_tail_small": LayerConfig("skew_tail_small", T=512, d=128, H=64, E=64, k=4, e_lo=20,
+                                   E_loc=8, bias="zipf"),
+}
+
+
+def compare_full(m, cfg, inp, R_cap=None):
+    idx, gates, perm = oracle_route_perm(inp, cfg)
+    buf, t = run_layer(m, cfg, inp, R_cap)
+    check_route_perm(buf, idx, gates, perm)
+    f = oracle.expert_layer_fwd(inp["x"], inp["w_gu"], inp["w_down"], perm, cfg.H, mode="S")
+    b = oracle.expert_layer_bwd(inp["x"], inp["dy"], inp["w_gu"], inp["w_down"], perm, cfg.H,
+                                mode="S")
+    R = perm["R"]
+    errs = dict(
+        h=rel_err(host_bf16(buf.h[:R]), f["h"]) if R else 0.0,
+        y=rel_err(host_bf16(buf.y), f["y"]),
+        dx=rel_err(host_bf16(buf.dx), b["dx"]),
+        dw_gu=rel_err(buf.dw_gu.cpu().numpy(), b["dw_gu"]),
+        dw_down=rel_err(buf.dw_down.cpu().numpy(), b["dw_down"]),
+        dp=rel_err(buf.dp.cpu().numpy(), b["dp"]),
+    )
+    if R:
+        errs["a"] = rel_err(host_bf16(buf.a[:R]), f["a"])
+    say(cfg.name, "R", R, {k: f"{v:.2e}" for k, v in errs.items()})
+    for k_, v in errs.items():
+        assert v <= (FP32_TOL if k_ == "dp" else BF16_TOL), (k_, v)
+    return buf, t, perm
+
+
+@pytest.mark.parametrize("name", list(SMALL_CASES))
+def test_layer_full(moe, name):
+    cfg = SMALL_CASES[name]
+    say(f"layer full {name}")
+    inp = layer_inputs(cfg, seed=0)
+    if name == "none_local":              # no token may pick the local window
+        inp["logits"][:, cfg.e_lo:cfg.e_lo + cfg.E_loc] -= 100.0
+    buf, t, perm = compare_full(moe, cfg, inp)
+    if name == "none_local":
+        assert perm["R"] == 0
+        assert not bool(buf.y.any()) and not bool(buf.dx.any()) and not bool(buf.dp.any())
+        assert not bool(buf.dw_gu.any()) and not bool(buf.dw_down.any())
+
+
+def test_layer_exact_capacity(moe):
+    """R_cap equal to the routed rows (the tightest legal buffers)."""
+    inp = layer_inputs(MID, seed=1)
+    _, _, perm = oracle_route_perm(inp, MID)
+    compare_full(moe, MID, inp, R_cap=perm["R"])
+
+
+def test_layer_deterministic_and_recompute_exact(moe):
+    """Repeat runs are bit-identical; the activation recomputed from h equals the stored one;
+    dy x 2 doubles dx, dW and dp exactly (power-of-two scaling is exact)."""
+    inp = layer_inputs(MID, seed=2)
+    buf, t = run_layer(moe, MID, inp)
+    R = buf.rows()
+    y1, dx1 = buf.y.clone(), buf.dx.clone()
+    dwg1, dwd1, dp1 = buf.dw_gu.clone(), buf.dw_down.clone(), buf.dp.clone()
+    a1 = buf.a[:R].clone()
+    buf.step(t["x"], t["logits"], t["w_gu"], t["w_down"], t["dy"])
+    torch.cuda.synchronize()
+    for u, v in ((y1, buf.y), (dx1, buf.dx), (dwg1, buf.dw_gu), (dwd1, buf.dw_down), (dp1, buf.dp)):
+        assert torch.equal(u, v)
+    a_re = moe.situ_glu_fwd(buf.h[:R].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(a_re.view(torch.int16), a1.view(torch.int16))
+    buf.backward(t["dy"] * 2, t["x"], t["w_gu"], t["w_down"])
+    torch.cuda.synchronize()
+    assert torch.equal(buf.dx.float(), dx1.float() * 2)
+    assert torch.equal(buf.dw_gu, dwg1 * 2) and torch.equal(buf.dw_down, dwd1 * 2)
+    assert torch.equal(buf.dp, dp1 * 2)
+
+
+def test_layer_token_permutation(moe):
+    """Permuting tokens permutes y and dx rows and leaves dW bit-identical."""
+    inp = layer_inputs(MID, seed=4)
+    buf, t = run_layer(moe, MID, inp)
+    y1, dx1, dw1 = buf.y.clone(), buf.dx.clone(), buf.dw_gu.clone()
+    perm_t = np.random.default_rng(0).permutation(MID.T)
+    inp2 = dict(inp)
+    for key in ("x", "logits", "dy"):
+        inp2[key] = inp[key][perm_t]
+    buf2, _ = run_layer(moe, MID, inp2)
+    pt = torch.from_numpy(perm_t).cuda()
+    assert torch.equal(buf2.y, y1[pt]) and torch.equal(buf2.dx, dx1[pt])
+    # dW sums rows in token order within an expert, which the permutation changes: compare
+    # to the bf16 bar instead of bitwise
+    assert rel_err(buf2.dw_gu.cpu().numpy(), dw1.cpu().numpy()) <= 1e-5
+
+
+# ------------------------------------------------------------------------------- layer, full-size sampled
+def compare_sampled(m, cfg, n_tok=48, n_exp=3, n_col=6, seed=0):
+    say(f"layer sampled {cfg.name}: generating inputs")
+    inp = layer_inputs(cfg, seed=0)
+    say(f"layer sampled {cfg.name}: oracle routing")
+    idx, gates, perm = oracle_route_perm(inp, cfg)
+    say(f"layer sampled {cfg.name}: GPU step (R={perm['R']})")
+    buf, t = run_layer(m, cfg, inp)
+    check_route_perm(buf, idx, gates, perm)
+    rng = np.random.default_rng(seed)
+    local_tok = np.unique(perm["row_token"]) if perm["R"] else np.zeros(0, int)
+    toks = np.concatenate([rng.choice(local_tok, min(n_tok, len(local_tok)), replace=False),
+                           rng.choice(cfg.T, 8, replace=False), [0, cfg.T - 1]])
+    sub, rows = sub_perm(perm, toks)
+    say(f"layer sampled {cfg.name}: oracle on {len(rows)} rows")
+    f = oracle.expert_layer_fwd(inp["x"], inp["w_gu"], inp["w_down"], sub, cfg.H, mode="S")
+    b = oracle.expert_layer_bwd(inp["x"], inp["dy"], inp["w_gu"], inp["w_down"], sub, cfg.H,
+                                mode="S")
+    toks = np.unique(toks)
+    tt = torch.from_numpy(toks).cuda()
+    rr = torch.from_numpy(rows).cuda()
+    errs = dict(
+        y=rel_err(host_bf16(buf.y[tt]), f["y"][toks]),
+        dx=rel_err(host_bf16(buf.dx[tt]), b["dx"][toks]),
+        dp=rel_err(buf.dp[tt].cpu().numpy(), b["dp"][toks]),
+        h=rel_err(host_bf16(buf.h[rr]), f["h"]),
+        a=rel_err(host_bf16(buf.a[rr]), f["a"]),
+    )
+    # weight gradients: sampled experts x intermediate columns (all rows of the expert)
+    counts = np.diff(perm["offsets"])
+    exps = list(rng.choice(cfg.E_loc, n_exp, replace=False))
+    if np.any(counts == 0):
+        exps.append(int(np.nonzero(counts == 0)[0][0]))
+    cols = np.unique(np.concatenate([rng.choice(cfg.H, n_col, replace=False), [0, cfg.H - 1]]))
+    dwg = buf.dw_gu
+    dwd = buf.dw_down
+    e_gu, e_dn = [], []
+    ref_gu_all, ref_dn_all, got_gu_all, got_dn_all = [], [], [], []
+    for e in exps:
+        say(f"layer sampled {cfg.name}: dW expert {e} rows {counts[e]}")
+        gu, dn = oracle.dw_columns(inp["x"], inp["dy"], inp["w_gu"], inp["w_down"], perm, int(e),
+                                   cols, cfg.H)
+        ci = torch.from_numpy(np.concatenate([cols, cfg.H + cols])).cuda()
+        got_gu_all.append(dwg[int(e)][ci].cpu().numpy())
+        got_dn_all.append(dwd[int(e)][:, torch.from_numpy(cols).cuda()].cpu().numpy())
+        ref_gu_all.append(gu)
+        ref_dn_all.append(dn)
+    errs["dw_gu"] = rel_err(np.stack(got_gu_all), np.stack(ref_gu_all))
+    errs["dw_down"] = rel_err(np.stack(got_dn_all), np.stack(ref_dn_all))
+    say(cfg.name, "R", perm["R"], {k: f"{v:.2e}" for k, v in errs.items()})
+    for k_, v in errs.items():
+        assert v <= (FP32_TOL if k_ == "dp" else BF16_TOL), (k_, v)
+    # properties over the whole tensors
+    nonlocal_tok = np.setdiff1d(np.arange(cfg.T), local_tok)
+    if len(nonlocal_tok):
+        nt = torch.from_numpy(nonlocal_tok).cuda()
+        assert not bool(buf.y[nt].any()) and not bool(buf.dx[nt].any())
+    for tname in ("y", "dx", "dp", "dw_gu", "dw_down"):
+        assert bool(torch.isfinite(getattr(buf, tname).float()).all()), tname
+    if np.any(counts == 0):
+        for e in np.nonzero(counts == 0)[0]:
+            assert not bool(dwg[int(e)].any()) and not bool(dwd[int(e)].any())
+
+
+@pytest.mark.parametrize("name", ["shard", "skew", "skew_mid", "skew_tail", "large"])
+def test_layer_full_size_sampled(moe, name):
+    compare_sampled(moe, LAYER_CONFIGS[name])
+    torch.cuda.empty_cache()
