@@ -111,7 +111,7 @@ __device__ __forceinline__ void store_kout(uint16_t* lds, const u32x4 (&reg)[KB]
 }
 
 template <int BM, int BN, bool KRAG, int BKIND, int EPI>
-__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(GemmArgs p) {
+__global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128) ? 1 : 2) void grouped_gemm_kernel(GemmArgs p) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int NA = BM / 32;        // 16-byte registers per lane for an A stage
@@ -239,6 +239,24 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(GemmArgs p) {
     const int b_kb = tid / (BN / 8);
 
     u32x4 ra[NA], rb[NB];
+    // Ragged-K operands: storage rows of the next stage's k rows (-1 past the group's end),
+    // fetched one stage ahead of their use so the gather-index load latency is hidden.
+    int ia[KRAG ? NA : 1], ib[KRAG ? NB : 1];
+    auto fetch_rows = [&](int kt) {
+      if constexpr (KRAG) {
+        const int kbase = kt * kBK;
+#pragma unroll
+        for (int kk = 0; kk < NA; ++kk) {
+          const int kg = kbase + a_kb * NA + kk;
+          ia[kk] = (kg < Kg) ? (p.a_gather ? p.a_gather[r0 + kg] : (r0 + kg)) : -1;
+        }
+#pragma unroll
+        for (int kk = 0; kk < NB; ++kk) {
+          const int kg = kbase + b_kb * NB + kk;
+          ib[kk] = (kg < Kg) ? (p.b_gather ? p.b_gather[r0 + kg] : (r0 + kg)) : -1;
+        }
+      }
+    };
     auto load_stage = [&](int kt) {
       const int kbase = kt * kBK;
       if constexpr (!KRAG) {
@@ -246,15 +264,9 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(GemmArgs p) {
         for (int i = 0; i < NA; ++i) ra[i] = *(const u32x4*)(a_ptr[i] + kbase);
       } else {
 #pragma unroll
-        for (int kk = 0; kk < NA; ++kk) {
-          const int kg = kbase + a_kb * NA + kk;
-          if (kg < Kg) {
-            const int srow = p.a_gather ? p.a_gather[r0 + kg] : (r0 + kg);
-            ra[kk] = *(const u32x4*)(p.A + (int64_t)srow * p.lda + a_col);
-          } else {
-            ra[kk] = u32x4{0u, 0u, 0u, 0u};
-          }
-        }
+        for (int kk = 0; kk < NA; ++kk)
+          ra[kk] = (ia[kk] >= 0) ? *(const u32x4*)(p.A + (int64_t)ia[kk] * p.lda + a_col)
+                                 : u32x4{0u, 0u, 0u, 0u};
       }
       if constexpr (BKIND == B_ROWS) {
 #pragma unroll
@@ -265,15 +277,9 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(GemmArgs p) {
           rb[kk] = *(const u32x4*)(Bg + (int64_t)(kbase + b_kb * NB + kk) * p.ldb + b_col);
       } else {
 #pragma unroll
-        for (int kk = 0; kk < NB; ++kk) {
-          const int kg = kbase + b_kb * NB + kk;
-          if (kg < Kg) {
-            const int srow = p.b_gather ? p.b_gather[r0 + kg] : (r0 + kg);
-            rb[kk] = *(const u32x4*)(p.B + (int64_t)srow * p.ldb + b_col);
-          } else {
-            rb[kk] = u32x4{0u, 0u, 0u, 0u};
-          }
-        }
+        for (int kk = 0; kk < NB; ++kk)
+          rb[kk] = (ib[kk] >= 0) ? *(const u32x4*)(p.B + (int64_t)ib[kk] * p.ldb + b_col)
+                                 : u32x4{0u, 0u, 0u, 0u};
       }
     };
     auto store_stage = [&](int buf) {
@@ -301,32 +307,49 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
+    // Per-lane LDS element offsets of the MFMA fragments (k16 step s, block i / j); the
+    // swizzle depends only on the row, so these are fixed for the whole tile.
+    constexpr int KS = kBK / 16;
+    int offa[KS][FM], offb[KS][FN];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int ch = 2 * s + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) offa[s][i] = lds_off(wm * WM + i * 32 + (lane & 31), ch);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) offb[s][j] = lds_off(wn * WN + j * 32 + (lane & 31), ch);
+    }
+    // All fragments of a stage are read before its MFMAs so the LDS latency of later k16
+    // steps hides behind the MFMAs of earlier ones.
     auto compute_stage = [&](int buf) {
+      bf16x8 af[KS][FM], bfr[KS][FN];
 #pragma unroll
-      for (int s = 0; s < kBK / 16; ++s) {
-        const int ch = 2 * s + (lane >> 5);
-        bf16x8 af[FM], bfr[FN];
+      for (int s = 0; s < KS; ++s) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-          af[i] = *(const bf16x8*)&sA[buf][lds_off(wm * WM + i * 32 + (lane & 31), ch)];
+        for (int i = 0; i < FM; ++i) af[s][i] = *(const bf16x8*)&sA[buf][offa[s][i]];
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          bfr[j] = *(const bf16x8*)&sB[buf][lds_off(wn * WN + j * 32 + (lane & 31), ch)];
+        for (int j = 0; j < FN; ++j) bfr[s][j] = *(const bf16x8*)&sB[buf][offb[s][j]];
+      }
+      __builtin_amdgcn_sched_barrier(0);     // keep every read ahead of the MFMAs
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      }
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s][i], bfr[s][j], acc[i][j], 0, 0, 0);
     };
 
     if (nk > 0) {
+      fetch_rows(0);
       load_stage(0);
+      if (nk > 1) fetch_rows(1);
       store_stage(0);
     }
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
       if (kt + 1 < nk) load_stage(kt + 1);
+      if (kt + 2 < nk) fetch_rows(kt + 2);
       compute_stage(kt & 1);
       if (kt + 1 < nk) store_stage((kt + 1) & 1);
       __syncthreads();
@@ -439,7 +462,28 @@ static hipError_t run_gemm(const GemmArgs& args, int64_t max_tiles, hipStream_t 
   return hipGetLastError();
 }
 
-constexpr int kTM = 128, kTN = 128;
+// Tile shapes per contraction (BM x BN); each must be 128 or 256.
+#ifndef MOE_TILE_GU
+#define MOE_TILE_GU 128, 128
+#endif
+#ifndef MOE_TILE_DN
+#define MOE_TILE_DN 128, 128
+#endif
+#ifndef MOE_TILE_DA
+#define MOE_TILE_DA 128, 128
+#endif
+#ifndef MOE_TILE_DX
+#define MOE_TILE_DX 128, 128
+#endif
+#ifndef MOE_TILE_WD
+#define MOE_TILE_WD 128, 128
+#endif
+#ifndef MOE_TILE_WG
+#define MOE_TILE_WG 128, 128
+#endif
+struct TileShape { int bm, bn; };
+constexpr TileShape kGU{MOE_TILE_GU}, kDN{MOE_TILE_DN}, kDA{MOE_TILE_DA}, kDX{MOE_TILE_DX},
+    kWD{MOE_TILE_WD}, kWG{MOE_TILE_WG};
 
 static GemmArgs blank_args() {
   GemmArgs a;
@@ -460,11 +504,11 @@ hipError_t launch_gemm_gate_up(const uint16_t* x, const int32_t* row_token,
   p.B = w_gu; p.ldb = d; p.b_gstride = (int64_t)2 * H * d;
   p.offsets = offsets; p.G = E_loc;
   p.N = 2 * H; p.K = d; p.H = H;
-  p.n_tiles = (H + kTN / 2 - 1) / (kTN / 2);
+  p.n_tiles = (H + kGU.bn / 2 - 1) / (kGU.bn / 2);
   p.o0 = h; p.ld0 = 2 * H; p.o1 = a; p.ld1 = H;
   p.sc = c;
-  return run_gemm<kTM, kTN, false, B_ROWS, EPI_GATEUP>(
-      p, mragged_tile_bound(R_cap, E_loc, kTM, p.n_tiles), s);
+  return run_gemm<kGU.bm, kGU.bn, false, B_ROWS, EPI_GATEUP>(
+      p, mragged_tile_bound(R_cap, E_loc, kGU.bm, p.n_tiles), s);
 }
 
 hipError_t launch_gemm_down(const uint16_t* a, const int32_t* offsets, const float* row_gate,
@@ -475,13 +519,13 @@ hipError_t launch_gemm_down(const uint16_t* a, const int32_t* offsets, const flo
   p.B = w_down; p.ldb = H; p.b_gstride = (int64_t)d * H;
   p.offsets = offsets; p.G = E_loc;
   p.N = d; p.K = H;
-  p.n_tiles = (d + kTN - 1) / kTN;
+  p.n_tiles = (d + kDN.bn - 1) / kDN.bn;
   p.o0 = rows_out; p.ld0 = d; p.row_scale = row_gate;
-  return run_gemm<kTM, kTN, false, B_ROWS, EPI_ROWS_SCALED>(
-      p, mragged_tile_bound(R_cap, E_loc, kTM, p.n_tiles), s);
+  return run_gemm<kDN.bm, kDN.bn, false, B_ROWS, EPI_ROWS_SCALED>(
+      p, mragged_tile_bound(R_cap, E_loc, kDN.bm, p.n_tiles), s);
 }
 
-int gemm_da_slots(int H) { return ((H + kTN - 1) / kTN) * 2; }
+int gemm_da_slots(int H) { return ((H + kDA.bn - 1) / kDA.bn) * 2; }
 
 hipError_t launch_gemm_da(const uint16_t* dy, const int32_t* row_token, const int32_t* offsets,
                           int E_loc, int64_t R_cap, int d, int H, const uint16_t* w_down,
@@ -492,12 +536,12 @@ hipError_t launch_gemm_da(const uint16_t* dy, const int32_t* row_token, const in
   p.B = w_down; p.ldb = H; p.b_gstride = (int64_t)d * H;      // B(n=j, k) = w_down[e][k][j]
   p.offsets = offsets; p.G = E_loc;
   p.N = H; p.K = d; p.H = H;
-  p.n_tiles = (H + kTN - 1) / kTN;
+  p.n_tiles = (H + kDA.bn - 1) / kDA.bn;
   p.o0 = dh; p.ld0 = 2 * H; p.o1 = pa; p.ld1 = H;
   p.row_scale = row_gate; p.hsrc = h; p.dp_part = dp_part; p.dp_ld = R_cap;
   p.sc = c;
-  return run_gemm<kTM, kTN, false, B_KOUT, EPI_DA>(
-      p, mragged_tile_bound(R_cap, E_loc, kTM, p.n_tiles), s);
+  return run_gemm<kDA.bm, kDA.bn, false, B_KOUT, EPI_DA>(
+      p, mragged_tile_bound(R_cap, E_loc, kDA.bm, p.n_tiles), s);
 }
 
 hipError_t launch_gemm_dx(const uint16_t* dh, const int32_t* offsets, int E_loc,
@@ -508,10 +552,10 @@ hipError_t launch_gemm_dx(const uint16_t* dh, const int32_t* offsets, int E_loc,
   p.B = w_gu; p.ldb = d; p.b_gstride = (int64_t)2 * H * d;    // B(n, k) = w_gu[e][k][n]
   p.offsets = offsets; p.G = E_loc;
   p.N = d; p.K = 2 * H;
-  p.n_tiles = (d + kTN - 1) / kTN;
+  p.n_tiles = (d + kDX.bn - 1) / kDX.bn;
   p.o0 = rows_out; p.ld0 = d;
-  return run_gemm<kTM, kTN, false, B_KOUT, EPI_ROWS>(
-      p, mragged_tile_bound(R_cap, E_loc, kTM, p.n_tiles), s);
+  return run_gemm<kDX.bm, kDX.bn, false, B_KOUT, EPI_ROWS>(
+      p, mragged_tile_bound(R_cap, E_loc, kDX.bm, p.n_tiles), s);
 }
 
 hipError_t launch_gemm_dw_down(const uint16_t* dy, const int32_t* row_token,
@@ -522,10 +566,10 @@ hipError_t launch_gemm_dw_down(const uint16_t* dy, const int32_t* row_token,
   p.B = pa; p.ldb = H;                                        // B(n, k=r) = pa[r][n]
   p.offsets = offsets; p.G = E_loc;
   p.M = d; p.N = H;
-  p.m_tiles = (d + kTM - 1) / kTM;
-  p.n_tiles = (H + kTN - 1) / kTN;
+  p.m_tiles = (d + kWD.bm - 1) / kWD.bm;
+  p.n_tiles = (H + kWD.bn - 1) / kWD.bn;
   p.of = dw_down; p.ldf = H; p.f_gstride = (int64_t)d * H;
-  return run_gemm<kTM, kTN, true, B_KOUT, EPI_F32>(
+  return run_gemm<kWD.bm, kWD.bn, true, B_KOUT, EPI_F32>(
       p, (int64_t)E_loc * p.m_tiles * p.n_tiles, s);
 }
 
@@ -537,10 +581,10 @@ hipError_t launch_gemm_dw_gu(const uint16_t* dh, const uint16_t* x, const int32_
   p.B = x; p.ldb = d; p.b_gather = row_token;                 // B(n, k=r) = x[tok(r)][n]
   p.offsets = offsets; p.G = E_loc;
   p.M = 2 * H; p.N = d;
-  p.m_tiles = (2 * H + kTM - 1) / kTM;
-  p.n_tiles = (d + kTN - 1) / kTN;
+  p.m_tiles = (2 * H + kWG.bm - 1) / kWG.bm;
+  p.n_tiles = (d + kWG.bn - 1) / kWG.bn;
   p.of = dw_gu; p.ldf = d; p.f_gstride = (int64_t)2 * H * d;
-  return run_gemm<kTM, kTN, true, B_KOUT, EPI_F32>(
+  return run_gemm<kWG.bm, kWG.bn, true, B_KOUT, EPI_F32>(
       p, (int64_t)E_loc * p.m_tiles * p.n_tiles, s);
 }
 
