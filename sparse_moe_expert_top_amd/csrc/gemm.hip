@@ -40,7 +40,8 @@
 
 namespace moe {
 
-constexpr int kBK = 64;              // bf16 elements of K per LDS stage
+constexpr int kBK = 32;              // bf16 elements of K per LDS stage
+constexpr int kNS = 4;               // stages in the LDS ring
 constexpr int kThreads = 256;
 
 enum BKind { B_ROWS = 0, B_KOUT = 1 };
@@ -74,53 +75,77 @@ struct GemmArgs {
   SituCoef sc;
 };
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * kBK + ((chunk ^ swz(row)) << 3);
+// ---------------------------------------------------------------------------- LDS stages
+// A K-contiguous ("rows") operand stage is [TR][kBK] bf16: 64-byte rows of four 16-byte
+// chunks, chunk c of row r at position c ^ ((r >> 1) & 3). Eight consecutive rows at one
+// logical chunk then fill the eight 16-byte slots of a 128-byte bank window, so the MFMA
+// fragment reads (ds_read_b128) are conflict-free.
+// A k-outer operand stage is [kBK][TR] bf16 (k-rows of TR columns), chunk c of k-row k at
+// position c ^ (4 (k & 1)): a transposing fragment read touches k-rows {k0..k0+3} and
+// {k0+8..k0+11} over four chunks, which this spreads evenly over the eight slots.
+// Stages are filled by direct-to-LDS loads (global_load_lds_dwordx4): a wave's load writes
+// 64 x 16 bytes contiguously, so each lane fetches the global chunk that belongs at its
+// position; the swizzle above is realised by that choice.
+__device__ __forceinline__ int rswz(int row) { return (row >> 1) & 3; }
+__device__ __forceinline__ int kswz(int k) { return (k & 1) << 2; }
+
+// Source of k-rows past the end of a ragged K extent (must read as zeros).
+__device__ __attribute__((aligned(16))) uint16_t g_zero_row[256];
+
+// One direct-to-LDS load: this lane's 16 bytes at `src` go to LDS byte address
+// lds_base + 16 * lane, lds_base being wave-uniform. Issued from inline assembly so the
+// compiler does not track it: its waitcnt pass cannot tell ring slots apart and would
+// otherwise drain every in-flight load before each LDS read. The kernel orders these loads
+// itself (explicit vmcnt waits plus barriers); M0 is saved and restored around the load.
+__device__ __forceinline__ void dma16(const uint16_t* src, const uint16_t* lds_dst) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_dst);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(base)
+      : "memory");
 }
 
-// Column c (0..7) of a pair of 8-wide rows, as one dword {x[c], y[c]}.
-__device__ __forceinline__ uint32_t pair_col(const u32x4& x, const u32x4& y, int c) {
-  const uint32_t a = x[c >> 1], b = y[c >> 1];
-  return (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+// Wait until at most N vector-memory operations of this wave are outstanding, and for all
+// of its LDS operations (gfx9 s_waitcnt: vmcnt[3:0,15:14], expcnt[6:4], lgkmcnt[11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
 }
 
-// Store a k-outer register block (KB rows of 8 columns, rows k0..k0+KB-1 of the stage,
-// columns col0..col0+7 of the tile) transposed into the [col][k] LDS tile.
-template <int KB>
-__device__ __forceinline__ void store_kout(uint16_t* lds, const u32x4 (&reg)[KB], int col0,
-                                           int k0) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int row = col0 + c;
-    if constexpr (KB == 8) {
-      u32x4 w;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) w[p] = pair_col(reg[2 * p], reg[2 * p + 1], c);
-      *(u32x4*)&lds[lds_off(row, k0 >> 3)] = w;
-    } else if constexpr (KB == 4) {
-      u32x2 w;
-#pragma unroll
-      for (int p = 0; p < 2; ++p) w[p] = pair_col(reg[2 * p], reg[2 * p + 1], c);
-      *(u32x2*)&lds[lds_off(row, k0 >> 3) + (k0 & 7)] = w;
-    } else {
-      static_assert(KB == 2, "k-outer block height");
-      *(uint32_t*)&lds[lds_off(row, k0 >> 3) + (k0 & 7)] = pair_col(reg[0], reg[1], 0 + c);
-    }
-  }
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16): within each 16-lane group, lane
+// i = 4a + b receives element b of the 4-element reads of lanes a, 4+a, 8+a, 12+a. When
+// lane s of a group points at k-row k0 + s/4, column m0 + 4 (s % 4) of a k-outer tile,
+// lane i receives k-rows k0..k0+3 of column m0 + i.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i16x4 ds_read_tr(const uint16_t* lds_src) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)lds_src);
 }
 
 template <int BM, int BN, bool KRAG, int BKIND, int EPI>
-__global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128) ? 1 : 2) void grouped_gemm_kernel(GemmArgs p) {
+__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(GemmArgs p) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int FM = WM / 32, FN = WN / 32;
-  constexpr int NA = BM / 32;        // 16-byte registers per lane for an A stage
-  constexpr int NB = BN / 32;        // ... for a B stage
+  constexpr bool A_KO = KRAG;                       // A k-outer (weight gradients)
+  constexpr bool B_KO = (BKIND == B_KOUT);
+  constexpr int LA = BM * kBK * 2 / 1024 / 4;       // direct-to-LDS loads per wave per stage
+  constexpr int LB = BN * kBK * 2 / 1024 / 4;
+  constexpr int LPS = LA + LB;
+  constexpr int NIDX = KRAG ? LPS : 0;              // gather-index loads per wave per stage
+  constexpr int KS = kBK / 16;                      // MFMA k-steps per stage
   static_assert(!KRAG || BKIND == B_KOUT, "weight gradients read B k-outer");
   static_assert(EPI != EPI_GATEUP || (FN % 2 == 0), "gate/linear pairs");
+  static_assert(LA >= 1 && LB >= 1 && kNS == 4, "stage geometry");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kBK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * kBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sA[kNS][BM * kBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB[kNS][BN * kBK];
   __shared__ int s_pref[1025];
   __shared__ int s_scan[kThreads];
 
@@ -167,6 +192,40 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128) ? 1 : 2) void group
     __syncthreads();
   }
 
+  // Per-lane fragment offsets inside a stage (element units).
+  int offa[KS][FM][2], offb[KS][FN][2];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if constexpr (!A_KO) {
+          const int row = wm * WM + i * 32 + (lane & 31);
+          offa[s][i][h] = row * kBK + (((2 * s + (lane >> 5)) ^ rswz(row)) << 3);
+        } else {
+          const int g16 = lane >> 4, i16 = lane & 15;
+          const int kr = s * 16 + 8 * (g16 >> 1) + 4 * h + (i16 >> 2);
+          const int col = wm * WM + i * 32 + (g16 & 1) * 16 + 4 * (i16 & 3);
+          offa[s][i][h] = kr * BM + (((col >> 3) ^ kswz(kr)) << 3) + (col & 7);
+        }
+      }
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if constexpr (!B_KO) {
+          const int row = wn * WN + j * 32 + (lane & 31);
+          offb[s][j][h] = row * kBK + (((2 * s + (lane >> 5)) ^ rswz(row)) << 3);
+        } else {
+          const int g16 = lane >> 4, i16 = lane & 15;
+          const int kr = s * 16 + 8 * (g16 >> 1) + 4 * h + (i16 >> 2);
+          const int col = wn * WN + j * 32 + (g16 & 1) * 16 + 4 * (i16 & 3);
+          offb[s][j][h] = kr * BN + (((col >> 3) ^ kswz(kr)) << 3) + (col & 7);
+        }
+      }
+  }
+
   const int nblk = gridDim.x;
   const int b = blockIdx.x;
   const int first = ((nblk & 7) == 0) ? ((b & 7) * (nblk >> 3) + (b >> 3)) : b;
@@ -200,103 +259,89 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128) ? 1 : 2) void group
     const int m0 = mt * BM;
     const int n0 = nt * BN;
     const int j0 = nt * (BN / 2);          // gate_up: first gate/linear column pair
-
-    // ------------------------------------------------------------ operand addressing
-    const uint16_t* a_ptr[NA];
-    int a_col = 0;
-    if constexpr (!KRAG) {
-#pragma unroll
-      for (int i = 0; i < NA; ++i) {
-        const int rr = (tid >> 3) + 32 * i;
-        const int m = min(m0 + rr, Mg - 1);
-        const int srow = p.a_gather ? p.a_gather[r0 + m] : (r0 + m);
-        a_ptr[i] = p.A + (int64_t)srow * p.lda + (tid & 7) * 8;
-      }
-    } else {
-      a_col = min(m0 + (tid % (BM / 8)) * 8, p.M - 8);
-    }
-    const uint16_t* b_ptr[NB];
-    int b_col = 0;
     const uint16_t* Bg = p.B + (int64_t)g * p.b_gstride;
-    if constexpr (BKIND == B_ROWS) {
+
+    // ------------------------------------------------------------ load addressing
+    // Load q of this wave fills bytes [(wave * L + q) * 1024, +1024) of a stage; lane L
+    // writes the 16 bytes at + 16 L.
+    const uint16_t* a_src[LA];   // rows: per-stage base (advance kBK per stage)
+    int a_kr[LA], a_col[LA];     // k-outer: k-row inside the stage and source column
+    const uint16_t* b_src[LB];
+    int b_kr[LB], b_col[LB];
 #pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const int nn = (tid >> 3) + 32 * i;
+    for (int q = 0; q < LA; ++q) {
+      const int byte = (wave * LA + q) * 1024 + lane * 16;
+      if constexpr (!A_KO) {
+        const int row = byte / (kBK * 2);
+        const int c = ((byte % (kBK * 2)) >> 4) ^ rswz(row);
+        const int m = min(m0 + row, Mg - 1);
+        const int srow = p.a_gather ? p.a_gather[r0 + m] : (r0 + m);
+        a_src[q] = p.A + (int64_t)srow * p.lda + c * 8;
+      } else {
+        const int kr = byte / (BM * 2);
+        const int c = ((byte % (BM * 2)) >> 4) ^ kswz(kr);
+        a_kr[q] = kr;
+        a_col[q] = min(m0 + c * 8, p.M - 8);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < LB; ++q) {
+      const int byte = (wave * LB + q) * 1024 + lane * 16;
+      if constexpr (!B_KO) {
+        const int row = byte / (kBK * 2);
+        const int c = ((byte % (kBK * 2)) >> 4) ^ rswz(row);
         int wrow;
         if constexpr (EPI == EPI_GATEUP) {
-          const int w = nn / WN, q = nn % WN;
-          const int jj = min(j0 + w * (WN / 2) + (q % (WN / 2)), p.H - 1);
-          wrow = (q < WN / 2) ? jj : p.H + jj;
+          const int w = row / WN, qq = row % WN;
+          const int jj = min(j0 + w * (WN / 2) + (qq % (WN / 2)), p.H - 1);
+          wrow = (qq < WN / 2) ? jj : p.H + jj;
         } else {
-          wrow = min(n0 + nn, p.N - 1);
+          wrow = min(n0 + row, p.N - 1);
         }
-        b_ptr[i] = Bg + (int64_t)wrow * p.ldb + (tid & 7) * 8;
+        b_src[q] = Bg + (int64_t)wrow * p.ldb + c * 8;
+      } else {
+        const int kr = byte / (BN * 2);
+        const int c = ((byte % (BN * 2)) >> 4) ^ kswz(kr);
+        b_kr[q] = kr;
+        b_col[q] = min(n0 + c * 8, p.N - 8);
       }
-    } else {
-      b_col = min(n0 + (tid % (BN / 8)) * 8, p.N - 8);
     }
-    const int a_kb = tid / (BM / 8);       // k-outer block index (rows a_kb*NA ..)
-    const int b_kb = tid / (BN / 8);
 
-    u32x4 ra[NA], rb[NB];
-    // Ragged-K operands: storage rows of the next stage's k rows (-1 past the group's end),
-    // fetched one stage ahead of their use so the gather-index load latency is hidden.
-    int ia[KRAG ? NA : 1], ib[KRAG ? NB : 1];
+    // Ragged-K operands: storage row of each load's k-row for the next stage to issue
+    // (-1 past the group's end), fetched one stage ahead of its use.
+    int ia[KRAG ? LA : 1], ib[KRAG ? LB : 1];
     auto fetch_rows = [&](int kt) {
       if constexpr (KRAG) {
-        const int kbase = kt * kBK;
 #pragma unroll
-        for (int kk = 0; kk < NA; ++kk) {
-          const int kg = kbase + a_kb * NA + kk;
-          ia[kk] = (kg < Kg) ? (p.a_gather ? p.a_gather[r0 + kg] : (r0 + kg)) : -1;
+        for (int q = 0; q < LA; ++q) {
+          const int kg = kt * kBK + a_kr[q];
+          ia[q] = (kg < Kg) ? (p.a_gather ? p.a_gather[r0 + kg] : (r0 + kg)) : -1;
         }
 #pragma unroll
-        for (int kk = 0; kk < NB; ++kk) {
-          const int kg = kbase + b_kb * NB + kk;
-          ib[kk] = (kg < Kg) ? (p.b_gather ? p.b_gather[r0 + kg] : (r0 + kg)) : -1;
+        for (int q = 0; q < LB; ++q) {
+          const int kg = kt * kBK + b_kr[q];
+          ib[q] = (kg < Kg) ? (p.b_gather ? p.b_gather[r0 + kg] : (r0 + kg)) : -1;
         }
       }
     };
-    auto load_stage = [&](int kt) {
-      const int kbase = kt * kBK;
-      if constexpr (!KRAG) {
+    auto issue = [&](int kt) {
+      const int slot = kt & (kNS - 1);
 #pragma unroll
-        for (int i = 0; i < NA; ++i) ra[i] = *(const u32x4*)(a_ptr[i] + kbase);
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < NA; ++kk)
-          ra[kk] = (ia[kk] >= 0) ? *(const u32x4*)(p.A + (int64_t)ia[kk] * p.lda + a_col)
-                                 : u32x4{0u, 0u, 0u, 0u};
+      for (int q = 0; q < LA; ++q) {
+        const uint16_t* src;
+        if constexpr (!A_KO) src = a_src[q] + kt * kBK;
+        else src = (ia[q] >= 0) ? p.A + (int64_t)ia[q] * p.lda + a_col[q] : g_zero_row;
+        dma16(src, &sA[slot][(wave * LA + q) * 512]);
       }
-      if constexpr (BKIND == B_ROWS) {
 #pragma unroll
-        for (int i = 0; i < NB; ++i) rb[i] = *(const u32x4*)(b_ptr[i] + kbase);
-      } else if constexpr (!KRAG) {
-#pragma unroll
-        for (int kk = 0; kk < NB; ++kk)
-          rb[kk] = *(const u32x4*)(Bg + (int64_t)(kbase + b_kb * NB + kk) * p.ldb + b_col);
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < NB; ++kk)
-          rb[kk] = (ib[kk] >= 0) ? *(const u32x4*)(p.B + (int64_t)ib[kk] * p.ldb + b_col)
-                                 : u32x4{0u, 0u, 0u, 0u};
+      for (int q = 0; q < LB; ++q) {
+        const uint16_t* src;
+        if constexpr (!B_KO) src = b_src[q] + kt * kBK;
+        else if constexpr (!KRAG) src = Bg + (int64_t)(kt * kBK + b_kr[q]) * p.ldb + b_col[q];
+        else src = (ib[q] >= 0) ? p.B + (int64_t)ib[q] * p.ldb + b_col[q] : g_zero_row;
+        dma16(src, &sB[slot][(wave * LB + q) * 512]);
       }
-    };
-    auto store_stage = [&](int buf) {
-      if constexpr (!KRAG) {
-#pragma unroll
-        for (int i = 0; i < NA; ++i)
-          *(u32x4*)&sA[buf][lds_off((tid >> 3) + 32 * i, tid & 7)] = ra[i];
-      } else {
-        store_kout<NA>(sA[buf], ra, (tid % (BM / 8)) * 8, a_kb * NA);
-      }
-      if constexpr (BKIND == B_ROWS) {
-#pragma unroll
-        for (int i = 0; i < NB; ++i)
-          *(u32x4*)&sB[buf][lds_off((tid >> 3) + 32 * i, tid & 7)] = rb[i];
-      } else {
-        store_kout<NB>(sB[buf], rb, (tid % (BN / 8)) * 8, b_kb * NB);
-      }
+      if (kt + 1 < nk) fetch_rows(kt + 1);
     };
 
     f32x16 acc[FM][FN];
@@ -307,30 +352,32 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128) ? 1 : 2) void group
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    // Per-lane LDS element offsets of the MFMA fragments (k16 step s, block i / j); the
-    // swizzle depends only on the row, so these are fixed for the whole tile.
-    constexpr int KS = kBK / 16;
-    int offa[KS][FM], offb[KS][FN];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int ch = 2 * s + (lane >> 5);
-#pragma unroll
-      for (int i = 0; i < FM; ++i) offa[s][i] = lds_off(wm * WM + i * 32 + (lane & 31), ch);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) offb[s][j] = lds_off(wn * WN + j * 32 + (lane & 31), ch);
-    }
-    // All fragments of a stage are read before its MFMAs so the LDS latency of later k16
-    // steps hides behind the MFMAs of earlier ones.
-    auto compute_stage = [&](int buf) {
+    auto compute_stage = [&](int slot) {
       bf16x8 af[KS][FM], bfr[KS][FN];
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i) af[s][i] = *(const bf16x8*)&sA[buf][offa[s][i]];
+        for (int i = 0; i < FM; ++i) {
+          if constexpr (!A_KO) {
+            af[s][i] = *(const bf16x8*)&sA[slot][offa[s][i][0]];
+          } else {
+            const i16x4 lo = ds_read_tr(&sA[slot][offa[s][i][0]]);
+            const i16x4 hi = ds_read_tr(&sA[slot][offa[s][i][1]]);
+            af[s][i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+        }
 #pragma unroll
-        for (int j = 0; j < FN; ++j) bfr[s][j] = *(const bf16x8*)&sB[buf][offb[s][j]];
+        for (int j = 0; j < FN; ++j) {
+          if constexpr (!B_KO) {
+            bfr[s][j] = *(const bf16x8*)&sB[slot][offb[s][j][0]];
+          } else {
+            const i16x4 lo = ds_read_tr(&sB[slot][offb[s][j][0]]);
+            const i16x4 hi = ds_read_tr(&sB[slot][offb[s][j][1]]);
+            bfr[s][j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+        }
       }
-      __builtin_amdgcn_sched_barrier(0);     // keep every read ahead of the MFMAs
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < KS; ++s)
 #pragma unroll
@@ -340,20 +387,29 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128) ? 1 : 2) void group
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s][i], bfr[s][j], acc[i][j], 0, 0, 0);
     };
 
-    if (nk > 0) {
-      fetch_rows(0);
-      load_stage(0);
-      if (nk > 1) fetch_rows(1);
-      store_stage(0);
-    }
-    __syncthreads();
+    // ------------------------------------------------------------ k pipeline
+    // kNS-stage ring: stages kt+1 .. kt+kNS-2 stay in flight while stage kt is consumed.
+    // Before stage kt is read: this wave's loads for it have landed (vmcnt) and every
+    // wave's have (barrier). The same barrier orders the refill of the slot consumed in
+    // the previous iteration after every wave's reads of it.
+    fetch_rows(0);
+#pragma unroll
+    for (int st = 0; st < kNS - 1; ++st)
+      if (st < nk) issue(st);
     for (int kt = 0; kt < nk; ++kt) {
-      if (kt + 1 < nk) load_stage(kt + 1);
-      if (kt + 2 < nk) fetch_rows(kt + 2);
-      compute_stage(kt & 1);
-      if (kt + 1 < nk) store_stage((kt + 1) & 1);
-      __syncthreads();
+      const int remaining = nk - 1 - kt;
+      if (remaining >= 2) wait_vm_lgkm0<2 * (LPS + NIDX)>();
+      else if (remaining == 1) wait_vm_lgkm0<LPS + NIDX>();
+      else wait_vm_lgkm0<0>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + kNS - 1 < nk) issue(kt + kNS - 1);
+      compute_stage(kt & (kNS - 1));
     }
+    // every wave is done with the ring before the next tile refills it
+    wait_vm_lgkm0<0>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
 
     // ------------------------------------------------------------ epilogues
     // acc[i][j][v] holds C[row][col] with row = i*32 + 8*(v/4) + 4*(lane/32) + v%4 and
