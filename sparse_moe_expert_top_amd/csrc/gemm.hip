@@ -76,18 +76,20 @@ struct GemmArgs {
 };
 
 // ---------------------------------------------------------------------------- LDS stages
+// LDS on gfx950 serves a 16-byte-per-lane read in 256-byte passes (64 banks of 4 bytes), so
+// a read is conflict-free when the 16 lanes of a pass hit 16 distinct 16-byte slots of a
+// 256-byte window.
 // A K-contiguous ("rows") operand stage is [TR][kBK] bf16: 64-byte rows of four 16-byte
-// chunks, chunk c of row r at position c ^ ((r >> 1) & 3). Eight consecutive rows at one
-// logical chunk then fill the eight 16-byte slots of a 128-byte bank window, so the MFMA
-// fragment reads (ds_read_b128) are conflict-free.
+// chunks, chunk c of row r at position c ^ ((r >> 2) & 3). Sixteen consecutive rows at one
+// logical chunk (an MFMA fragment read) then land in sixteen distinct slots.
 // A k-outer operand stage is [kBK][TR] bf16 (k-rows of TR columns), chunk c of k-row k at
-// position c ^ (4 (k & 1)): a transposing fragment read touches k-rows {k0..k0+3} and
-// {k0+8..k0+11} over four chunks, which this spreads evenly over the eight slots.
+// position c ^ (4 (k & 3)): a transposing fragment read covers four consecutive k-rows of
+// four chunks per pass, which this maps to sixteen distinct slots.
 // Stages are filled by direct-to-LDS loads (global_load_lds_dwordx4): a wave's load writes
 // 64 x 16 bytes contiguously, so each lane fetches the global chunk that belongs at its
 // position; the swizzle above is realised by that choice.
-__device__ __forceinline__ int rswz(int row) { return (row >> 1) & 3; }
-__device__ __forceinline__ int kswz(int k) { return (k & 1) << 2; }
+__device__ __forceinline__ int rswz(int row) { return (row >> 2) & 3; }
+__device__ __forceinline__ int kswz(int k) { return (k & 3) << 2; }
 
 // Source of k-rows past the end of a ragged K extent (must read as zeros).
 __device__ __attribute__((aligned(16))) uint16_t g_zero_row[256];
@@ -130,7 +132,7 @@ __device__ __forceinline__ i16x4 ds_read_tr(const uint16_t* lds_src) {
 }
 
 template <int BM, int BN, bool KRAG, int BKIND, int EPI>
-__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(GemmArgs p) {
+__global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128) ? 1 : 2) void grouped_gemm_kernel(GemmArgs p) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr bool A_KO = KRAG;                       // A k-outer (weight gradients)
