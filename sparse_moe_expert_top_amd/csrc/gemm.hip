@@ -14,20 +14,24 @@
 //   dW_gu     sum_r dh[r]^T x[tok(r)]         2H       d     rows    k-outer      k-outer+g
 //
 // Design (gfx950):
-//  * v_mfma_f32_32x32x16_bf16, fp32 accumulators; 4 wavefronts per workgroup in a 2x2 grid,
-//    each owning a (BM/2) x (BN/2) block of C.
-//  * Operands are staged through LDS as [row][64 k] bf16 tiles (two stages, one barrier per
-//    k-step). The 16-byte chunk c of row r sits at chunk position c ^ ((r ^ r>>3) & 7), so
-//    the MFMA fragment reads (8 consecutive rows, same chunk) and the transposing stores
-//    (rows 8 apart, same chunk) both hit distinct banks.
-//  * "rows" operands are K-contiguous in HBM and load 16 bytes per lane, optionally through a
-//    row index (the dispatch gather). "k-outer" operands are stored with K as the outer
-//    index; each lane loads a (BM/32)-row x 8-column block and transposes it in registers
-//    (byte permutes) before the LDS store, so every MFMA reads K-contiguous fragments.
+//  * v_mfma_f32_32x32x16_bf16 with fp32 accumulators. A workgroup of WGM x WGN wavefronts
+//    owns a BM x BN tile; each wavefront a (BM/WGM) x (BN/WGN) block of it. The large
+//    configuration (256 x 256, 8 wavefronts, two per SIMD) loads 8 bytes per kFLOP.
+//  * K advances in stages of BK through an NS-slot LDS ring. Each stage is filled by
+//    direct-to-LDS loads (global_load_lds_dwordx4, 1 KiB per wavefront instruction), issued
+//    NS-1 stages ahead of its use; one barrier per stage orders fills after the reads of
+//    the slot they overwrite.
+//  * "rows" operands (K contiguous in HBM) stay [row][BK] in LDS, with an XOR swizzle of the
+//    16-byte chunks; each lane loads the chunk that belongs at its LDS position, optionally
+//    through a row index (the dispatch gather). MFMA fragments are ds_read_b128.
+//  * "k-outer" operands (K the outer index in HBM) stay [k][row] in LDS and are read with
+//    the transposing ds_read_b64_tr_b16, so no operand is ever transposed in registers.
+//    Ragged-K tails read a zero row.
 //  * Ragged extents come from the device-side expert offsets: a persistent grid walks a tile
-//    list built in LDS from those offsets (no host sync). Consecutive tile ids go to the
-//    same XCD (workgroup i runs on XCD i mod 8), so the m-tiles sharing one expert's weight
-//    panel run together and share that XCD's L2.
+//    list built in LDS from those offsets (no host sync). Inside an expert, tiles go in
+//    GROUP_M super-rows (all n-tiles of group_m m-tiles, m fastest), and consecutive tile
+//    ids go to one XCD (workgroup i runs on XCD i mod 8), so tiles running together on an
+//    XCD share both operand panels in its L2.
 //  * Epilogues: gate_up writes h (bf16) and a = bf16(SiTU-GLU(bf16 h)); down writes
 //    bf16(p * o) rows for the combine; dA recomputes a from the saved h, accumulates the
 //    per-row <G, a> partials, and writes dh and bf16(p a); dX writes bf16 rows; the weight
@@ -39,10 +43,6 @@
 #include "situ_math.h"
 
 namespace moe {
-
-constexpr int kBK = 32;              // bf16 elements of K per LDS stage
-constexpr int kNS = 4;               // stages in the LDS ring
-constexpr int kThreads = 256;
 
 enum BKind { B_ROWS = 0, B_KOUT = 1 };
 enum Epi { EPI_GATEUP = 0, EPI_ROWS_SCALED = 1, EPI_ROWS = 2, EPI_DA = 3, EPI_F32 = 4 };
@@ -61,6 +61,7 @@ struct GemmArgs {
   int H;             // split of the gate/linear halves (gate_up, dA)
   int n_tiles;       // tiles along N (gate_up: along the H gate/linear column pairs)
   int m_tiles;       // tiles along M (weight gradients)
+  int group_m;       // m-tiles per rasterization super-row
   uint16_t* o0;
   int64_t ld0;
   uint16_t* o1;
@@ -75,33 +76,49 @@ struct GemmArgs {
   SituCoef sc;
 };
 
+// Tile configuration: BM x BN tile, WGM x WGN wavefronts, BK-deep stages, NS-slot ring,
+// WPE = wavefronts per SIMD the kernel is compiled for.
+template <int BM_, int BN_, int WGM_, int WGN_, int BK_, int NS_, int WPE_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, BK = BK_, NS = NS_;
+  static constexpr int WPE = WPE_;
+  static constexpr int NT = 64 * WGM * WGN;
+};
+using CfgBig = TileCfg<256, 256, 2, 4, 64, 2, 2>;     // 8 waves, 128 KiB ring, 1 WG per CU
+using CfgMid = TileCfg<128, 256, 2, 4, 64, 2, 2>;     // 8 waves, 96 KiB ring
+using CfgSmall = TileCfg<128, 128, 2, 2, 32, 4, 2>;   // 4 waves, 64 KiB ring, 2 WG per CU
+
 // ---------------------------------------------------------------------------- LDS stages
 // LDS on gfx950 serves a 16-byte-per-lane read in 256-byte passes (64 banks of 4 bytes), so
 // a read is conflict-free when the 16 lanes of a pass hit 16 distinct 16-byte slots of a
 // 256-byte window.
-// A K-contiguous ("rows") operand stage is [TR][kBK] bf16: 64-byte rows of four 16-byte
-// chunks, chunk c of row r at position c ^ ((r >> 2) & 3). Sixteen consecutive rows at one
-// logical chunk (an MFMA fragment read) then land in sixteen distinct slots.
-// A k-outer operand stage is [kBK][TR] bf16 (k-rows of TR columns), chunk c of k-row k at
+// A "rows" stage is [TR][BK] bf16. With BK = 64 a row is 128 bytes and chunk c of row r sits
+// at position c ^ ((r >> 1) & 7); with BK = 32 a row is 64 bytes and chunk c sits at
+// c ^ ((r >> 2) & 3). Sixteen consecutive rows at one logical chunk (a fragment read) then
+// land in sixteen distinct slots.
+// A "k-outer" stage is [BK][TR] bf16 (k-rows of TR >= 128 columns), chunk c of k-row k at
 // position c ^ (4 (k & 3)): a transposing fragment read covers four consecutive k-rows of
 // four chunks per pass, which this maps to sixteen distinct slots.
-// Stages are filled by direct-to-LDS loads (global_load_lds_dwordx4): a wave's load writes
-// 64 x 16 bytes contiguously, so each lane fetches the global chunk that belongs at its
-// position; the swizzle above is realised by that choice.
-__device__ __forceinline__ int rswz(int row) { return (row >> 2) & 3; }
+// Direct-to-LDS loads write a wavefront's 64 x 16 bytes contiguously, so the swizzle is
+// realised by which global chunk each lane fetches.
+template <int BK>
+__device__ __forceinline__ int rswz(int row) {
+  if constexpr (BK == 64) return (row >> 1) & 7;
+  else return (row >> 2) & 3;
+}
 __device__ __forceinline__ int kswz(int k) { return (k & 3) << 2; }
 
 // Source of k-rows past the end of a ragged K extent (must read as zeros).
 __device__ __attribute__((aligned(16))) uint16_t g_zero_row[256];
 
-// One direct-to-LDS load: this lane's 16 bytes at `src` go to LDS byte address
-// lds_base + 16 * lane, lds_base being wave-uniform. Issued from inline assembly so the
-// compiler does not track it: its waitcnt pass cannot tell ring slots apart and would
+// Direct-to-LDS loads (global_load_lds_dwordx4): each lane's 16 bytes land at LDS byte
+// address M0 + 16 * lane, M0 being wave-uniform. They are issued from inline assembly so the
+// compiler does not track them: its waitcnt pass cannot tell ring slots apart and would
 // otherwise drain every in-flight load before each LDS read. The kernel orders these loads
-// itself (explicit vmcnt waits plus barriers); M0 is saved and restored around the load.
-__device__ __forceinline__ void dma16(const uint16_t* src, const uint16_t* lds_dst) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_dst);
+// itself (explicit vmcnt waits plus barriers); M0 is saved and restored around them.
+//
+// dma_vaddr: one load from a per-lane 64-bit address.
+__device__ __forceinline__ void dma_vaddr(const uint16_t* src, uint32_t lds_addr) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -109,8 +126,50 @@ __device__ __forceinline__ void dma16(const uint16_t* src, const uint16_t* lds_d
       "global_load_lds_dwordx4 %1, off\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(src), "s"(base)
+      : "v"(src), "s"(lds_addr)
       : "memory");
+}
+// dma_saddr: L loads from a wave-uniform 64-bit base plus per-lane 32-bit byte offsets;
+// load q lands at lds0 + 1024 q.
+template <int L>
+__device__ __forceinline__ void dma_saddr(uint32_t lds0, const void* sbase,
+                                          const uint32_t (&voff)[L]) {
+  uint32_t saved;
+  if constexpr (L == 2) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "global_load_lds_dwordx4 %4, %3\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %5, %3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds0), "s"(lds0 + 1024u), "s"(sbase), "v"(voff[0]), "v"(voff[1])
+        : "memory");
+  } else {
+    static_assert(L == 4, "loads per operand per stage");
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "global_load_lds_dwordx4 %6, %5\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %7, %5\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "global_load_lds_dwordx4 %8, %5\n\t"
+        "s_mov_b32 m0, %4\n\t"
+        "global_load_lds_dwordx4 %9, %5\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds0), "s"(lds0 + 1024u), "s"(lds0 + 2048u), "s"(lds0 + 3072u), "s"(sbase),
+          "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3])
+        : "memory");
+  }
+}
+__device__ __forceinline__ const void* uniform_ptr(const void* ptr) {
+  const uint64_t a = (uint64_t)(uintptr_t)ptr;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding, and for all
@@ -131,41 +190,50 @@ __device__ __forceinline__ i16x4 ds_read_tr(const uint16_t* lds_src) {
       (__attribute__((address_space(3))) i16x4*)lds_src);
 }
 
-template <int BM, int BN, bool KRAG, int BKIND, int EPI>
-__global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128) ? 1 : 2) void grouped_gemm_kernel(GemmArgs p) {
-  constexpr int WM = BM / 2, WN = BN / 2;
+template <class C, bool KRAG, int BKIND, int EPI>
+__global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p) {
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, NS = C::NS, NT = C::NT, NW = NT / 64;
+  constexpr int WM = BM / C::WGM, WN = BN / C::WGN;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr bool A_KO = KRAG;                       // A k-outer (weight gradients)
   constexpr bool B_KO = (BKIND == B_KOUT);
-  constexpr int LA = BM * kBK * 2 / 1024 / 4;       // direct-to-LDS loads per wave per stage
-  constexpr int LB = BN * kBK * 2 / 1024 / 4;
+  constexpr int LA = BM * BK * 2 / 1024 / NW;       // direct-to-LDS loads per wave per stage
+  constexpr int LB = BN * BK * 2 / 1024 / NW;
   constexpr int LPS = LA + LB;
   constexpr int NIDX = KRAG ? LPS : 0;              // gather-index loads per wave per stage
-  constexpr int KS = kBK / 16;                      // MFMA k-steps per stage
+  constexpr int KS = BK / 16;                       // MFMA k-steps per stage
+  constexpr int GPT = (1024 + NT - 1) / NT;         // expert offsets per thread in the scan
+  static_assert(LA * 1024 * NW == BM * BK * 2 && LB * 1024 * NW == BN * BK * 2, "loads");
+  static_assert(LA >= 1 && LB >= 1 && (NS == 2 || NS == 4), "stage geometry");
   static_assert(!KRAG || BKIND == B_KOUT, "weight gradients read B k-outer");
   static_assert(EPI != EPI_GATEUP || (FN % 2 == 0), "gate/linear pairs");
-  static_assert(LA >= 1 && LB >= 1 && kNS == 4, "stage geometry");
+  static_assert(BK == 32 || BK == 64, "stage depth");
 
-  __shared__ __attribute__((aligned(1024))) uint16_t sA[kNS][BM * kBK];
-  __shared__ __attribute__((aligned(1024))) uint16_t sB[kNS][BN * kBK];
+  // One LDS ring for both operands; after the k-loop it doubles as the epilogue's staging.
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[NS * (BM + BN) * BK];
+  uint16_t (*sA)[BM * BK] = reinterpret_cast<uint16_t (*)[BM * BK]>(ring);
+  uint16_t (*sB)[BN * BK] = reinterpret_cast<uint16_t (*)[BN * BK]>(ring + NS * BM * BK);
   __shared__ int s_pref[1025];
-  __shared__ int s_scan[kThreads];
+  __shared__ int s_scan[NT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ring);
 
   // ---------------------------------------------------------------- tile list
   int total;
   if constexpr (KRAG) {
     total = p.G * p.m_tiles * p.n_tiles;
   } else {
-    int loc[4];
+    int loc[GPT];
     int sum = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int g = tid * 4 + i;
+    for (int i = 0; i < GPT; ++i) {
+      const int g = tid * GPT + i;
       int c = 0;
       if (g < p.G) {
         const int mg = p.offsets[g + 1] - p.offsets[g];
@@ -176,7 +244,7 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128) ? 1 : 2) void group
     }
     s_scan[tid] = sum;
     __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
+    for (int off = 1; off < NT; off <<= 1) {
       const int v = (tid >= off) ? s_scan[tid - off] : 0;
       __syncthreads();
       s_scan[tid] += v;
@@ -184,47 +252,59 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128) ? 1 : 2) void group
     }
     int run = s_scan[tid] - sum;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int g = tid * 4 + i;
+    for (int i = 0; i < GPT; ++i) {
+      const int g = tid * GPT + i;
       if (g < p.G) s_pref[g] = run;
       run += loc[i];
     }
-    total = s_scan[kThreads - 1];
+    total = s_scan[NT - 1];
     if (tid == 0) s_pref[p.G] = total;
     __syncthreads();
   }
 
-  // Per-lane fragment offsets inside a stage (element units).
-  int offa[KS][FM][2], offb[KS][FN][2];
+  // GROUP_M rasterization of a tile inside its expert: super-rows of group_m m-tiles, each
+  // swept over all n-tiles with the m index fastest.
+  auto raster = [&](int local, int mtiles, int &mt, int &nt) {
+    const int gm = p.group_m;
+    const int per_super = gm * p.n_tiles;
+    const int sr = local / per_super;
+    const int rem = local - sr * per_super;
+    const int rows = min(gm, mtiles - sr * gm);
+    nt = rem / rows;
+    mt = sr * gm + (rem - nt * rows);
+  };
+
+  // Per-lane fragment offsets inside a stage (element units): offset = base[i] + step[s][h].
+  int abase[FM], bbase[FN], astep[KS][2], bstep[KS][2];
+  {
+    const int g16 = lane >> 4, i16 = lane & 15;
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if constexpr (!A_KO) {
-          const int row = wm * WM + i * 32 + (lane & 31);
-          offa[s][i][h] = row * kBK + (((2 * s + (lane >> 5)) ^ rswz(row)) << 3);
-        } else {
-          const int g16 = lane >> 4, i16 = lane & 15;
-          const int kr = s * 16 + 8 * (g16 >> 1) + 4 * h + (i16 >> 2);
-          const int col = wm * WM + i * 32 + (g16 & 1) * 16 + 4 * (i16 & 3);
-          offa[s][i][h] = kr * BM + (((col >> 3) ^ kswz(kr)) << 3) + (col & 7);
-        }
+    for (int i = 0; i < FM; ++i) {
+      if constexpr (!A_KO) {
+        abase[i] = (wm * WM + i * 32 + (lane & 31)) * BK;
+      } else {
+        const int chunk = (wm * WM + i * 32 + (g16 & 1) * 16) / 8 + ((i16 & 3) >> 1);
+        abase[i] = (8 * (g16 >> 1) + (i16 >> 2)) * BM + ((chunk ^ kswz(i16 >> 2)) << 3) +
+                   4 * (i16 & 1);
       }
+    }
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+    for (int j = 0; j < FN; ++j) {
+      if constexpr (!B_KO) {
+        bbase[j] = (wn * WN + j * 32 + (lane & 31)) * BK;
+      } else {
+        const int chunk = (wn * WN + j * 32 + (g16 & 1) * 16) / 8 + ((i16 & 3) >> 1);
+        bbase[j] = (8 * (g16 >> 1) + (i16 >> 2)) * BN + ((chunk ^ kswz(i16 >> 2)) << 3) +
+                   4 * (i16 & 1);
+      }
+    }
+    const int rsw = rswz<BK>(lane & 31);
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        if constexpr (!B_KO) {
-          const int row = wn * WN + j * 32 + (lane & 31);
-          offb[s][j][h] = row * kBK + (((2 * s + (lane >> 5)) ^ rswz(row)) << 3);
-        } else {
-          const int g16 = lane >> 4, i16 = lane & 15;
-          const int kr = s * 16 + 8 * (g16 >> 1) + 4 * h + (i16 >> 2);
-          const int col = wn * WN + j * 32 + (g16 & 1) * 16 + 4 * (i16 & 3);
-          offb[s][j][h] = kr * BN + (((col >> 3) ^ kswz(kr)) << 3) + (col & 7);
-        }
+        astep[s][h] = A_KO ? (s * 16 + 4 * h) * BM : (((2 * s + (lane >> 5)) ^ rsw) << 3);
+        bstep[s][h] = B_KO ? (s * 16 + 4 * h) * BN : (((2 * s + (lane >> 5)) ^ rsw) << 3);
       }
   }
 
@@ -237,9 +317,7 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128) ? 1 : 2) void group
     if constexpr (KRAG) {
       const int per = p.m_tiles * p.n_tiles;
       g = tile / per;
-      const int rem = tile - g * per;
-      nt = rem / p.m_tiles;
-      mt = rem - nt * p.m_tiles;
+      raster(tile - g * per, p.m_tiles, mt, nt);
     } else {
       int lo = 0, hi = p.G;
       while (hi - lo > 1) {
@@ -248,16 +326,16 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128) ? 1 : 2) void group
       }
       g = lo;
       const int mg = p.offsets[g + 1] - p.offsets[g];
-      const int mtg = (mg + BM - 1) / BM;
-      const int local = tile - s_pref[g];
-      nt = local / mtg;
-      mt = local - nt * mtg;
+      raster(tile - s_pref[g], (mg + BM - 1) / BM, mt, nt);
     }
+    g = __builtin_amdgcn_readfirstlane(g);
+    mt = __builtin_amdgcn_readfirstlane(mt);
+    nt = __builtin_amdgcn_readfirstlane(nt);
     const int r0 = p.offsets[g];
     const int gcount = p.offsets[g + 1] - r0;
     const int Mg = KRAG ? p.M : gcount;
     const int Kg = KRAG ? gcount : p.K;
-    const int nk = (Kg + kBK - 1) / kBK;
+    const int nk = (Kg + BK - 1) / BK;
     const int m0 = mt * BM;
     const int n0 = nt * BN;
     const int j0 = nt * (BN / 2);          // gate_up: first gate/linear column pair
@@ -266,19 +344,22 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128) ? 1 : 2) void group
     // ------------------------------------------------------------ load addressing
     // Load q of this wave fills bytes [(wave * L + q) * 1024, +1024) of a stage; lane L
     // writes the 16 bytes at + 16 L.
-    const uint16_t* a_src[LA];   // rows: per-stage base (advance kBK per stage)
-    int a_kr[LA], a_col[LA];     // k-outer: k-row inside the stage and source column
-    const uint16_t* b_src[LB];
+    // Rows and fixed-K k-outer operands: wave-uniform base (advanced per stage) plus a
+    // per-lane 32-bit byte offset. Ragged-K k-outer operands: k-row and column per load.
+    uint32_t a_off[LA], b_off[LB];
+    int a_kr[LA], a_col[LA];
     int b_kr[LB], b_col[LB];
+    // rows of A: gathered rows are addressed from A itself, contiguous rows from row r0
+    const uint16_t* a_base = p.a_gather ? p.A : p.A + (int64_t)r0 * p.lda;
 #pragma unroll
     for (int q = 0; q < LA; ++q) {
       const int byte = (wave * LA + q) * 1024 + lane * 16;
       if constexpr (!A_KO) {
-        const int row = byte / (kBK * 2);
-        const int c = ((byte % (kBK * 2)) >> 4) ^ rswz(row);
+        const int row = byte / (BK * 2);
+        const int c = ((byte % (BK * 2)) >> 4) ^ rswz<BK>(row);
         const int m = min(m0 + row, Mg - 1);
-        const int srow = p.a_gather ? p.a_gather[r0 + m] : (r0 + m);
-        a_src[q] = p.A + (int64_t)srow * p.lda + c * 8;
+        const int srow = p.a_gather ? p.a_gather[r0 + m] : m;
+        a_off[q] = (uint32_t)(((int64_t)srow * p.lda + c * 8) * 2);
       } else {
         const int kr = byte / (BM * 2);
         const int c = ((byte % (BM * 2)) >> 4) ^ kswz(kr);
@@ -290,8 +371,8 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128) ? 1 : 2) void group
     for (int q = 0; q < LB; ++q) {
       const int byte = (wave * LB + q) * 1024 + lane * 16;
       if constexpr (!B_KO) {
-        const int row = byte / (kBK * 2);
-        const int c = ((byte % (kBK * 2)) >> 4) ^ rswz(row);
+        const int row = byte / (BK * 2);
+        const int c = ((byte % (BK * 2)) >> 4) ^ rswz<BK>(row);
         int wrow;
         if constexpr (EPI == EPI_GATEUP) {
           const int w = row / WN, qq = row % WN;
@@ -300,12 +381,13 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128) ? 1 : 2) void group
         } else {
           wrow = min(n0 + row, p.N - 1);
         }
-        b_src[q] = Bg + (int64_t)wrow * p.ldb + c * 8;
+        b_off[q] = (uint32_t)(((int64_t)wrow * p.ldb + c * 8) * 2);
       } else {
         const int kr = byte / (BN * 2);
         const int c = ((byte % (BN * 2)) >> 4) ^ kswz(kr);
         b_kr[q] = kr;
         b_col[q] = min(n0 + c * 8, p.N - 8);
+        b_off[q] = (uint32_t)(((int64_t)kr * p.ldb + b_col[q]) * 2);
       }
     }
 
@@ -316,32 +398,37 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128) ? 1 : 2) void group
       if constexpr (KRAG) {
 #pragma unroll
         for (int q = 0; q < LA; ++q) {
-          const int kg = kt * kBK + a_kr[q];
+          const int kg = kt * BK + a_kr[q];
           ia[q] = (kg < Kg) ? (p.a_gather ? p.a_gather[r0 + kg] : (r0 + kg)) : -1;
         }
 #pragma unroll
         for (int q = 0; q < LB; ++q) {
-          const int kg = kt * kBK + b_kr[q];
+          const int kg = kt * BK + b_kr[q];
           ib[q] = (kg < Kg) ? (p.b_gather ? p.b_gather[r0 + kg] : (r0 + kg)) : -1;
         }
       }
     };
     auto issue = [&](int kt) {
-      const int slot = kt & (kNS - 1);
+      const int slot = kt & (NS - 1);
+      const uint32_t lds_a = ring_lds + slot * (BM * BK * 2) + wave_u * (LA * 1024);
+      const uint32_t lds_b = ring_lds + NS * (BM * BK * 2) + slot * (BN * BK * 2) + wave_u * (LB * 1024);
+      if constexpr (!A_KO) {
+        dma_saddr<LA>(lds_a, uniform_ptr(a_base + kt * BK), a_off);
+      } else {
 #pragma unroll
-      for (int q = 0; q < LA; ++q) {
-        const uint16_t* src;
-        if constexpr (!A_KO) src = a_src[q] + kt * kBK;
-        else src = (ia[q] >= 0) ? p.A + (int64_t)ia[q] * p.lda + a_col[q] : g_zero_row;
-        dma16(src, &sA[slot][(wave * LA + q) * 512]);
+        for (int q = 0; q < LA; ++q)
+          dma_vaddr((ia[q] >= 0) ? p.A + (int64_t)ia[q] * p.lda + a_col[q] : g_zero_row,
+                    lds_a + q * 1024);
       }
+      if constexpr (!B_KO) {
+        dma_saddr<LB>(lds_b, uniform_ptr(Bg + kt * BK), b_off);
+      } else if constexpr (!KRAG) {
+        dma_saddr<LB>(lds_b, uniform_ptr(Bg + (int64_t)kt * BK * p.ldb), b_off);
+      } else {
 #pragma unroll
-      for (int q = 0; q < LB; ++q) {
-        const uint16_t* src;
-        if constexpr (!B_KO) src = b_src[q] + kt * kBK;
-        else if constexpr (!KRAG) src = Bg + (int64_t)(kt * kBK + b_kr[q]) * p.ldb + b_col[q];
-        else src = (ib[q] >= 0) ? p.B + (int64_t)ib[q] * p.ldb + b_col[q] : g_zero_row;
-        dma16(src, &sB[slot][(wave * LB + q) * 512]);
+        for (int q = 0; q < LB; ++q)
+          dma_vaddr((ib[q] >= 0) ? p.B + (int64_t)ib[q] * p.ldb + b_col[q] : g_zero_row,
+                    lds_b + q * 1024);
       }
       if (kt + 1 < nk) fetch_rows(kt + 1);
     };
@@ -354,59 +441,62 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128) ? 1 : 2) void group
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    auto compute_stage = [&](int slot) {
-      bf16x8 af[KS][FM], bfr[KS][FN];
+    auto load_frags = [&](int slot, int s, bf16x8 (&af)[FM], bf16x8 (&bfr)[FN]) {
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          if constexpr (!A_KO) {
-            af[s][i] = *(const bf16x8*)&sA[slot][offa[s][i][0]];
-          } else {
-            const i16x4 lo = ds_read_tr(&sA[slot][offa[s][i][0]]);
-            const i16x4 hi = ds_read_tr(&sA[slot][offa[s][i][1]]);
-            af[s][i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          if constexpr (!B_KO) {
-            bfr[s][j] = *(const bf16x8*)&sB[slot][offb[s][j][0]];
-          } else {
-            const i16x4 lo = ds_read_tr(&sB[slot][offb[s][j][0]]);
-            const i16x4 hi = ds_read_tr(&sB[slot][offb[s][j][1]]);
-            bfr[s][j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          }
+      for (int i = 0; i < FM; ++i) {
+        if constexpr (!A_KO) {
+          af[i] = *(const bf16x8*)&sA[slot][abase[i] + astep[s][0]];
+        } else {
+          const i16x4 lo = ds_read_tr(&sA[slot][abase[i] + astep[s][0]]);
+          const i16x4 hi = ds_read_tr(&sA[slot][abase[i] + astep[s][1]]);
+          af[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int s = 0; s < KS; ++s)
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (!B_KO) {
+          bfr[j] = *(const bf16x8*)&sB[slot][bbase[j] + bstep[s][0]];
+        } else {
+          const i16x4 lo = ds_read_tr(&sB[slot][bbase[j] + bstep[s][0]]);
+          const i16x4 hi = ds_read_tr(&sB[slot][bbase[j] + bstep[s][1]]);
+          bfr[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      }
+    };
+    // Fragments of k-step s+1 are read while the MFMAs of step s run.
+    auto compute_stage = [&](int slot) {
+      bf16x8 fa[2][FM], fb[2][FN];
+      load_frags(slot, 0, fa[0], fb[0]);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        if (s + 1 < KS) load_frags(slot, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s][i], bfr[s][j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][i], fb[s & 1][j],
+                                                                acc[i][j], 0, 0, 0);
+      }
     };
 
     // ------------------------------------------------------------ k pipeline
-    // kNS-stage ring: stages kt+1 .. kt+kNS-2 stay in flight while stage kt is consumed.
-    // Before stage kt is read: this wave's loads for it have landed (vmcnt) and every
-    // wave's have (barrier). The same barrier orders the refill of the slot consumed in
-    // the previous iteration after every wave's reads of it.
+    // Stages kt+1 .. kt+NS-2 stay in flight while stage kt is consumed. Before stage kt is
+    // read, this wave's loads for it have landed (vmcnt) and every wave's have (barrier);
+    // the same barrier orders the refill of the slot consumed in the previous iteration
+    // after every wave's reads of it.
     fetch_rows(0);
 #pragma unroll
-    for (int st = 0; st < kNS - 1; ++st)
+    for (int st = 0; st < NS - 1; ++st)
       if (st < nk) issue(st);
     for (int kt = 0; kt < nk; ++kt) {
-      const int remaining = nk - 1 - kt;
-      if (remaining >= 2) wait_vm_lgkm0<2 * (LPS + NIDX)>();
-      else if (remaining == 1) wait_vm_lgkm0<LPS + NIDX>();
+      const int later = min(NS - 2, nk - 1 - kt);   // stages issued after kt
+      if (later >= 2) wait_vm_lgkm0<2 * (LPS + NIDX)>();
+      else if (later == 1) wait_vm_lgkm0<LPS + NIDX>();
       else wait_vm_lgkm0<0>();
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      if (kt + kNS - 1 < nk) issue(kt + kNS - 1);
-      compute_stage(kt & (kNS - 1));
+      if (kt + NS - 1 < nk) issue(kt + NS - 1);
+      compute_stage(kt & (NS - 1));
     }
     // every wave is done with the ring before the next tile refills it
     wait_vm_lgkm0<0>();
@@ -414,138 +504,191 @@ __global__ __launch_bounds__(kThreads, (BM * BN > 128 * 128) ? 1 : 2) void group
     __builtin_amdgcn_sched_barrier(0);
 
     // ------------------------------------------------------------ epilogues
-    // acc[i][j][v] holds C[row][col] with row = i*32 + 8*(v/4) + 4*(lane/32) + v%4 and
-    // col = j*32 + lane%32 inside the wavefront's block.
-    const int col_l = lane & 31;
-    const int rq = (lane >> 5) * 4;
+    // Each wavefront stages one 32-row block of its accumulators at a time in LDS (fp32,
+    // row stride EPS = WN + 8 floats, so rows r and r + 4 fall in opposite bank halves), then
+    // re-reads it row-major: every lane owns 8 consecutive columns of a row, so global loads
+    // and stores are 16 bytes wide. acc[i][j][v] holds row i*32 + 8*(v/4) + 4*(lane/32) +
+    // v%4 and column j*32 + lane%32 of the wavefront's block.
     if constexpr (EPI == EPI_F32) {
+      // fp32 weight gradients: 32 lanes already write 128 contiguous bytes of a row, so the
+      // accumulators go straight to memory.
       float* Cg = p.of + (int64_t)g * p.f_gstride;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          const int col = n0 + wn * WN + j * 32 + col_l;
+          const int col = n0 + wn * WN + j * 32 + (lane & 31);
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int row = m0 + wm * WM + i * 32 + (v >> 2) * 8 + rq + (v & 3);
+            const int row = m0 + wm * WM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
             if (row < p.M && col < p.N) Cg[(int64_t)row * p.ldf + col] = acc[i][j][v];
           }
         }
-    } else if constexpr (EPI == EPI_ROWS || EPI == EPI_ROWS_SCALED) {
+    } else {
+    constexpr int EPS = WN + 8;
+    static_assert(WN == 64, "epilogue lane mapping assumes 64-column wavefront blocks");
+    static_assert(NW * 32 * EPS * 4 <= NS * (BM + BN) * BK * 2, "epilogue staging fits the ring");
+    float* st = reinterpret_cast<float*>(ring) + wave * 32 * EPS;
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = m0 + wm * WM + i * 32 + (v >> 2) * 8 + rq + (v & 3);
-          if (row >= Mg) continue;
-          const int64_t r = r0 + row;
-          float sc = 1.0f;
-          if constexpr (EPI == EPI_ROWS_SCALED) sc = p.row_scale[r];
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int col = n0 + wn * WN + j * 32 + col_l;
-            if (col < p.N) p.o0[r * p.ld0 + col] = f32_to_bf16(acc[i][j][v] * sc);
+        for (int v = 0; v < 16; ++v)
+          st[((v >> 2) * 8 + (lane >> 5) * 4 + (v & 3)) * EPS + j * 32 + (lane & 31)] = acc[i][j][v];
+      const int rblk = m0 + wm * WM + i * 32;            // tile-relative row of block row 0
+      if constexpr (EPI == EPI_GATEUP) {
+        // lane: 8 gate columns (cc) of row (ps*16 + lane/4) and the matching 8 linear columns
+        const int cc = lane & 3;
+#pragma unroll
+        for (int ps = 0; ps < 2; ++ps) {
+          const int row = ps * 16 + (lane >> 2);
+          const int jj = j0 + wn * (WN / 2) + cc * 8;
+          const f32x4 g0 = *(const f32x4*)&st[row * EPS + cc * 8];
+          const f32x4 g1 = *(const f32x4*)&st[row * EPS + cc * 8 + 4];
+          const f32x4 l0 = *(const f32x4*)&st[row * EPS + 32 + cc * 8];
+          const f32x4 l1 = *(const f32x4*)&st[row * EPS + 32 + cc * 8 + 4];
+          if (rblk + row < Mg && jj < p.H) {
+            const int64_t r = r0 + rblk + row;
+            const float gv[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
+            const float lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+            u32x4 hg, hl, av;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              hg[q] = pack_bf16x2(gv[2 * q], gv[2 * q + 1]);
+              hl[q] = pack_bf16x2(lv[2 * q], lv[2 * q + 1]);
+              av[q] = pack_bf16x2(situ_fwd(bf16_lo(hg[q]), bf16_lo(hl[q]), p.sc),
+                                  situ_fwd(bf16_hi(hg[q]), bf16_hi(hl[q]), p.sc));
+            }
+            *(u32x4*)&p.o0[r * p.ld0 + jj] = hg;
+            *(u32x4*)&p.o0[r * p.ld0 + p.H + jj] = hl;
+            *(u32x4*)&p.o1[r * p.ld1 + jj] = av;
           }
         }
-    } else if constexpr (EPI == EPI_GATEUP) {
+      } else {
+        // lane: columns cc*8 .. cc*8+7 of row ps*8 + lane/8
+        const int cc = lane & 7;
+        const int col = n0 + wn * WN + cc * 8;
+        float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+        for (int ps = 0; ps < 4; ++ps) {
+          const int row = ps * 8 + (lane >> 3);
+          const f32x4 c0 = *(const f32x4*)&st[row * EPS + cc * 8];
+          const f32x4 c1 = *(const f32x4*)&st[row * EPS + cc * 8 + 4];
+          const float cv[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+          if constexpr (EPI == EPI_ROWS || EPI == EPI_ROWS_SCALED) {
+            if (rblk + row < Mg && col < p.N) {
+              const int64_t r = r0 + rblk + row;
+              float sc = 1.0f;
+              if constexpr (EPI == EPI_ROWS_SCALED) sc = p.row_scale[r];
+              u32x4 o;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = m0 + wm * WM + i * 32 + (v >> 2) * 8 + rq + (v & 3);
-          if (row >= Mg) continue;
-          const int64_t r = r0 + row;
-#pragma unroll
-          for (int j = 0; j < FN / 2; ++j) {
-            const int jj = j0 + wn * (WN / 2) + j * 32 + col_l;
-            if (jj >= p.H) continue;
-            const uint16_t hg = f32_to_bf16(acc[i][j][v]);
-            const uint16_t hl = f32_to_bf16(acc[i][j + FN / 2][v]);
-            p.o0[r * p.ld0 + jj] = hg;
-            p.o0[r * p.ld0 + p.H + jj] = hl;
-            p.o1[r * p.ld1 + jj] = f32_to_bf16(situ_fwd(bf16_to_f32(hg), bf16_to_f32(hl), p.sc));
-          }
-        }
-    } else if constexpr (EPI == EPI_DA) {
-      const int slot = nt * 2 + wn;
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = m0 + wm * WM + i * 32 + (v >> 2) * 8 + rq + (v & 3);
-          const bool vr = row < Mg;
-          const int64_t r = r0 + (vr ? row : 0);
-          const float pr = vr ? p.row_scale[r] : 0.0f;
-          float part = 0.0f;
-#pragma unroll
-          for (int j = 0; j < FN; ++j) {
-            const int n = n0 + wn * WN + j * 32 + col_l;
-            if (vr && n < p.N) {
-              const float gv = acc[i][j][v];
+              for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(cv[2 * q] * sc, cv[2 * q + 1] * sc);
+              *(u32x4*)&p.o0[r * p.ld0 + col] = o;
+            }
+          } else if constexpr (EPI == EPI_DA) {
+            if (rblk + row < Mg && col < p.N) {
+              const int64_t r = r0 + rblk + row;
+              const float pr = p.row_scale[r];
               const uint16_t* hr = p.hsrc + r * (2 * (int64_t)p.H);
-              float a, dgv, dlv;
-              situ_bwd(bf16_to_f32(hr[n]), bf16_to_f32(hr[p.H + n]), pr * gv, p.sc, a, dgv, dlv);
-              const float ab = round_bf16(a);
-              part += gv * ab;
+              const u32x4 hg = *(const u32x4*)&hr[col];
+              const u32x4 hl = *(const u32x4*)&hr[p.H + col];
+              u32x4 og, ol, oa;
+              float acc_p = 0.0f;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                float a0, dg0, dl0, a1, dg1, dl1;
+                situ_bwd(bf16_lo(hg[q]), bf16_lo(hl[q]), pr * cv[2 * q], p.sc, a0, dg0, dl0);
+                situ_bwd(bf16_hi(hg[q]), bf16_hi(hl[q]), pr * cv[2 * q + 1], p.sc, a1, dg1, dl1);
+                const float ab0 = round_bf16(a0), ab1 = round_bf16(a1);
+                acc_p += cv[2 * q] * ab0;
+                acc_p += cv[2 * q + 1] * ab1;
+                og[q] = pack_bf16x2(dg0, dg1);
+                ol[q] = pack_bf16x2(dl0, dl1);
+                oa[q] = pack_bf16x2(pr * ab0, pr * ab1);
+              }
               uint16_t* dr = p.o0 + r * p.ld0;
-              dr[n] = f32_to_bf16(dgv);
-              dr[p.H + n] = f32_to_bf16(dlv);
-              p.o1[r * p.ld1 + n] = f32_to_bf16(pr * ab);
+              *(u32x4*)&dr[col] = og;
+              *(u32x4*)&dr[p.H + col] = ol;
+              *(u32x4*)&p.o1[r * p.ld1 + col] = oa;
+              part[ps] = acc_p;
             }
           }
-          // sum over the 32 lanes that share this row
-#pragma unroll
-          for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
-          if (vr && col_l == 0) p.dp_part[(int64_t)slot * p.dp_ld + r] = part;
         }
+        if constexpr (EPI == EPI_DA) {
+          // <G, a> over this wavefront's 64 columns: sum the 8 lanes that share a row
+          const int slot = nt * C::WGN + wn;
+#pragma unroll
+          for (int ps = 0; ps < 4; ++ps) {
+            float v = part[ps];
+            v += __shfl_xor(v, 1, 64);
+            v += __shfl_xor(v, 2, 64);
+            v += __shfl_xor(v, 4, 64);
+            const int row = ps * 8 + (lane >> 3);
+            if (cc == 0 && rblk + row < Mg) p.dp_part[(int64_t)slot * p.dp_ld + r0 + rblk + row] = v;
+          }
+        }
+      }
     }
+    }
+    // the next tile refills the ring only after every wave has read its staging
+    wait_vm_lgkm0<0>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // ---------------------------------------------------------------------------- launchers
-template <int BM, int BN, bool KRAG, int BKIND, int EPI>
+template <class C, bool KRAG, int BKIND, int EPI>
 static hipError_t run_gemm(const GemmArgs& args, int64_t max_tiles, hipStream_t s) {
-  auto kern = grouped_gemm_kernel<BM, BN, KRAG, BKIND, EPI>;
+  auto kern = grouped_gemm_kernel<C, KRAG, BKIND, EPI>;
   static int occ = -1;                   // workgroups per CU for this instantiation
   if (occ < 0) {
     int o = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, kThreads, 0) != hipSuccess || o < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, kern, C::NT, 0) != hipSuccess || o < 1)
       o = 1;
     occ = o;
   }
   int64_t grid = (int64_t)device_cu_count() * occ;
   if (max_tiles < grid) grid = max_tiles;
   if (grid < 1) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), 0, s, args);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NT), 0, s, args);
   return hipGetLastError();
 }
 
-// Tile shapes per contraction (BM x BN); each must be 128 or 256.
-#ifndef MOE_TILE_GU
-#define MOE_TILE_GU 128, 128
+// Tile configuration per contraction.
+#ifndef MOE_CFG_GU
+#define MOE_CFG_GU CfgBig
 #endif
-#ifndef MOE_TILE_DN
-#define MOE_TILE_DN 128, 128
+#ifndef MOE_CFG_DN
+#define MOE_CFG_DN CfgBig
 #endif
-#ifndef MOE_TILE_DA
-#define MOE_TILE_DA 128, 128
+#ifndef MOE_CFG_DA
+#define MOE_CFG_DA CfgMid
 #endif
-#ifndef MOE_TILE_DX
-#define MOE_TILE_DX 128, 128
+#ifndef MOE_CFG_DX
+#define MOE_CFG_DX CfgBig
 #endif
-#ifndef MOE_TILE_WD
-#define MOE_TILE_WD 128, 128
+#ifndef MOE_CFG_WD
+#define MOE_CFG_WD CfgBig
 #endif
-#ifndef MOE_TILE_WG
-#define MOE_TILE_WG 128, 128
+#ifndef MOE_CFG_WG
+#define MOE_CFG_WG CfgBig
 #endif
-struct TileShape { int bm, bn; };
-constexpr TileShape kGU{MOE_TILE_GU}, kDN{MOE_TILE_DN}, kDA{MOE_TILE_DA}, kDX{MOE_TILE_DX},
-    kWD{MOE_TILE_WD}, kWG{MOE_TILE_WG};
+#ifndef MOE_GROUP_M
+#define MOE_GROUP_M 4
+#endif
+using CGU = MOE_CFG_GU;
+using CDN = MOE_CFG_DN;
+using CDA = MOE_CFG_DA;
+using CDX = MOE_CFG_DX;
+using CWD = MOE_CFG_WD;
+using CWG = MOE_CFG_WG;
 
 static GemmArgs blank_args() {
   GemmArgs a;
   __builtin_memset(&a, 0, sizeof(a));
+  a.group_m = MOE_GROUP_M;
   return a;
 }
 
@@ -562,11 +705,11 @@ hipError_t launch_gemm_gate_up(const uint16_t* x, const int32_t* row_token,
   p.B = w_gu; p.ldb = d; p.b_gstride = (int64_t)2 * H * d;
   p.offsets = offsets; p.G = E_loc;
   p.N = 2 * H; p.K = d; p.H = H;
-  p.n_tiles = (H + kGU.bn / 2 - 1) / (kGU.bn / 2);
+  p.n_tiles = (H + CGU::BN / 2 - 1) / (CGU::BN / 2);
   p.o0 = h; p.ld0 = 2 * H; p.o1 = a; p.ld1 = H;
   p.sc = c;
-  return run_gemm<kGU.bm, kGU.bn, false, B_ROWS, EPI_GATEUP>(
-      p, mragged_tile_bound(R_cap, E_loc, kGU.bm, p.n_tiles), s);
+  return run_gemm<CGU, false, B_ROWS, EPI_GATEUP>(
+      p, mragged_tile_bound(R_cap, E_loc, CGU::BM, p.n_tiles), s);
 }
 
 hipError_t launch_gemm_down(const uint16_t* a, const int32_t* offsets, const float* row_gate,
@@ -577,13 +720,13 @@ hipError_t launch_gemm_down(const uint16_t* a, const int32_t* offsets, const flo
   p.B = w_down; p.ldb = H; p.b_gstride = (int64_t)d * H;
   p.offsets = offsets; p.G = E_loc;
   p.N = d; p.K = H;
-  p.n_tiles = (d + kDN.bn - 1) / kDN.bn;
+  p.n_tiles = (d + CDN::BN - 1) / CDN::BN;
   p.o0 = rows_out; p.ld0 = d; p.row_scale = row_gate;
-  return run_gemm<kDN.bm, kDN.bn, false, B_ROWS, EPI_ROWS_SCALED>(
-      p, mragged_tile_bound(R_cap, E_loc, kDN.bm, p.n_tiles), s);
+  return run_gemm<CDN, false, B_ROWS, EPI_ROWS_SCALED>(
+      p, mragged_tile_bound(R_cap, E_loc, CDN::BM, p.n_tiles), s);
 }
 
-int gemm_da_slots(int H) { return ((H + kDA.bn - 1) / kDA.bn) * 2; }
+int gemm_da_slots(int H) { return ((H + CDA::BN - 1) / CDA::BN) * CDA::WGN; }
 
 hipError_t launch_gemm_da(const uint16_t* dy, const int32_t* row_token, const int32_t* offsets,
                           int E_loc, int64_t R_cap, int d, int H, const uint16_t* w_down,
@@ -594,12 +737,12 @@ hipError_t launch_gemm_da(const uint16_t* dy, const int32_t* row_token, const in
   p.B = w_down; p.ldb = H; p.b_gstride = (int64_t)d * H;      // B(n=j, k) = w_down[e][k][j]
   p.offsets = offsets; p.G = E_loc;
   p.N = H; p.K = d; p.H = H;
-  p.n_tiles = (H + kDA.bn - 1) / kDA.bn;
+  p.n_tiles = (H + CDA::BN - 1) / CDA::BN;
   p.o0 = dh; p.ld0 = 2 * H; p.o1 = pa; p.ld1 = H;
   p.row_scale = row_gate; p.hsrc = h; p.dp_part = dp_part; p.dp_ld = R_cap;
   p.sc = c;
-  return run_gemm<kDA.bm, kDA.bn, false, B_KOUT, EPI_DA>(
-      p, mragged_tile_bound(R_cap, E_loc, kDA.bm, p.n_tiles), s);
+  return run_gemm<CDA, false, B_KOUT, EPI_DA>(
+      p, mragged_tile_bound(R_cap, E_loc, CDA::BM, p.n_tiles), s);
 }
 
 hipError_t launch_gemm_dx(const uint16_t* dh, const int32_t* offsets, int E_loc,
@@ -610,10 +753,10 @@ hipError_t launch_gemm_dx(const uint16_t* dh, const int32_t* offsets, int E_loc,
   p.B = w_gu; p.ldb = d; p.b_gstride = (int64_t)2 * H * d;    // B(n, k) = w_gu[e][k][n]
   p.offsets = offsets; p.G = E_loc;
   p.N = d; p.K = 2 * H;
-  p.n_tiles = (d + kDX.bn - 1) / kDX.bn;
+  p.n_tiles = (d + CDX::BN - 1) / CDX::BN;
   p.o0 = rows_out; p.ld0 = d;
-  return run_gemm<kDX.bm, kDX.bn, false, B_KOUT, EPI_ROWS>(
-      p, mragged_tile_bound(R_cap, E_loc, kDX.bm, p.n_tiles), s);
+  return run_gemm<CDX, false, B_KOUT, EPI_ROWS>(
+      p, mragged_tile_bound(R_cap, E_loc, CDX::BM, p.n_tiles), s);
 }
 
 hipError_t launch_gemm_dw_down(const uint16_t* dy, const int32_t* row_token,
@@ -624,11 +767,10 @@ hipError_t launch_gemm_dw_down(const uint16_t* dy, const int32_t* row_token,
   p.B = pa; p.ldb = H;                                        // B(n, k=r) = pa[r][n]
   p.offsets = offsets; p.G = E_loc;
   p.M = d; p.N = H;
-  p.m_tiles = (d + kWD.bm - 1) / kWD.bm;
-  p.n_tiles = (H + kWD.bn - 1) / kWD.bn;
+  p.m_tiles = (d + CWD::BM - 1) / CWD::BM;
+  p.n_tiles = (H + CWD::BN - 1) / CWD::BN;
   p.of = dw_down; p.ldf = H; p.f_gstride = (int64_t)d * H;
-  return run_gemm<kWD.bm, kWD.bn, true, B_KOUT, EPI_F32>(
-      p, (int64_t)E_loc * p.m_tiles * p.n_tiles, s);
+  return run_gemm<CWD, true, B_KOUT, EPI_F32>(p, (int64_t)E_loc * p.m_tiles * p.n_tiles, s);
 }
 
 hipError_t launch_gemm_dw_gu(const uint16_t* dh, const uint16_t* x, const int32_t* row_token,
@@ -639,11 +781,10 @@ hipError_t launch_gemm_dw_gu(const uint16_t* dh, const uint16_t* x, const int32_
   p.B = x; p.ldb = d; p.b_gather = row_token;                 // B(n, k=r) = x[tok(r)][n]
   p.offsets = offsets; p.G = E_loc;
   p.M = 2 * H; p.N = d;
-  p.m_tiles = (2 * H + kWG.bm - 1) / kWG.bm;
-  p.n_tiles = (d + kWG.bn - 1) / kWG.bn;
+  p.m_tiles = (2 * H + CWG::BM - 1) / CWG::BM;
+  p.n_tiles = (d + CWG::BN - 1) / CWG::BN;
   p.of = dw_gu; p.ldf = d; p.f_gstride = (int64_t)2 * H * d;
-  return run_gemm<kWG.bm, kWG.bn, true, B_KOUT, EPI_F32>(
-      p, (int64_t)E_loc * p.m_tiles * p.n_tiles, s);
+  return run_gemm<CWG, true, B_KOUT, EPI_F32>(p, (int64_t)E_loc * p.m_tiles * p.n_tiles, s);
 }
 
 }  // namespace moe
