@@ -26,7 +26,9 @@
  *     output contents are unchanged. After MOE_ERR_HIP, moe_last_hip_error() gives the
  *     hipError_t of the failed launch on the calling thread.
  *   - Pointers to bf16/fp32 tensors must be 16-byte aligned; d and H must be multiples of
- *     64; k <= 32; E <= 1024; E_loc <= 1024.
+ *     64; k <= 32; E <= 1024; E_loc <= 1024. Token-indexed tensors must span less than
+ *     4 GiB per row block: T * max(d, 2H) * 2 < 2^32 (checked where T is an argument; for
+ *     moe_grouped_gemm_gate_up it is a precondition on x).
  *   - Routed rows R are data-dependent and stay on the device in expert_offsets[E_loc].
  *     Buffers indexed by rows are sized by a caller-chosen capacity R_cap (T*k always
  *     suffices). moe_permute clamps the offsets to R_cap and raises *status_flag when the

@@ -46,6 +46,13 @@ static bool layer_dims_ok(int d, int H) {
   return d > 0 && H > 0 && d % 64 == 0 && H % 64 == 0 && d <= (1 << 16) && H <= (1 << 16);
 }
 
+// The GEMMs address token rows and one expert's rows with 32-bit byte offsets: a [T, d],
+// [T, 2H] or [T, H] row block must span less than 4 GiB.
+static bool rows_addressable(int64_t T, int d, int H) {
+  const int64_t w = (int64_t)(d > 2 * H ? d : 2 * H);
+  return T * w * 2 < ((int64_t)1 << 32);
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -188,7 +195,7 @@ moe_status moe_grouped_gemm_down_combine(const void* a, const int32_t* expert_of
   if (T < 0 || k < 1 || E_loc < 1 || R_cap < 0) return MOE_ERR_SHAPE;
   if (k > 32 || E_loc > 1024 || !layer_dims_ok(d, H) || R_cap >= (int64_t)1 << 31)
     return MOE_ERR_UNSUPPORTED;
-  if (T * (int64_t)k >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  if (T * (int64_t)k >= (int64_t)1 << 31 || !rows_addressable(T, d, H)) return MOE_ERR_UNSUPPORTED;
   if (!expert_offsets || !w_down) return MOE_ERR_NULL;
   if (T > 0 && (!slot_row || !y)) return MOE_ERR_NULL;
   if (R_cap > 0 && (!a || !row_gate || !ws)) return MOE_ERR_NULL;
@@ -217,7 +224,7 @@ moe_status moe_expert_bwd(const void* dy, const void* x, const void* h,
   if (T < 0 || k < 1 || E_loc < 1 || R_cap < 0) return MOE_ERR_SHAPE;
   if (k > 32 || E_loc > 1024 || !layer_dims_ok(d, H) || R_cap >= (int64_t)1 << 31)
     return MOE_ERR_UNSUPPORTED;
-  if (T * (int64_t)k >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  if (T * (int64_t)k >= (int64_t)1 << 31 || !rows_addressable(T, d, H)) return MOE_ERR_UNSUPPORTED;
   if (!(beta > 0.0f) || !(linear_beta > 0.0f)) return MOE_ERR_SHAPE;
   if (!expert_offsets || !w_gu || !w_down || !dw_gu || !dw_down) return MOE_ERR_NULL;
   if (T > 0 && (!dy || !x || !slot_row || !dx || !dp)) return MOE_ERR_NULL;

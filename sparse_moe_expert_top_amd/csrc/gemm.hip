@@ -10,8 +10,8 @@
 //   down      a[r] . w_down[e]^T              rows     d     H       rows         rows (NT)
 //   dA        dy[tok(r)] . w_down[e]          rows     H     d       rows+gather  k-outer (NN)
 //   dX        dh[r] . w_gu[e]                 rows     d     2H      rows         k-outer (NN)
-//   dW_down   sum_r dy[tok(r)]^T pa[r]        d        H     rows    k-outer+g    k-outer (TN)
-//   dW_gu     sum_r dh[r]^T x[tok(r)]         2H       d     rows    k-outer      k-outer+g
+//   dW_down^T sum_r pa[r]^T dy[tok(r)]        H        d     rows    k-outer      k-outer+g (TN)
+//   dW_gu^T   sum_r x[tok(r)]^T dh[r]         d        2H    rows    k-outer+g    k-outer (TN)
 //
 // Design (gfx950):
 //  * v_mfma_f32_32x32x16_bf16 with fp32 accumulators. A workgroup of WGM x WGN wavefronts
@@ -35,7 +35,7 @@
 //  * Epilogues: gate_up writes h (bf16) and a = bf16(SiTU-GLU(bf16 h)); down writes
 //    bf16(p * o) rows for the combine; dA recomputes a from the saved h, accumulates the
 //    per-row <G, a> partials, and writes dh and bf16(p a); dX writes bf16 rows; the weight
-//    gradients write fp32 (zeros for experts without rows).
+//    gradients write fp32 rows (zeros for experts without rows).
 #include <hip/hip_runtime.h>
 
 #include "common.h"
@@ -365,6 +365,8 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
         const int c = ((byte % (BM * 2)) >> 4) ^ kswz(kr);
         a_kr[q] = kr;
         a_col[q] = min(m0 + c * 8, p.M - 8);
+        // full stages: gathered rows add idx * lda at issue; contiguous rows are fixed here
+        a_off[q] = (uint32_t)(((p.a_gather ? 0 : (int64_t)kr * p.lda) + a_col[q]) * 2);
       }
     }
 #pragma unroll
@@ -387,7 +389,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
         const int c = ((byte % (BN * 2)) >> 4) ^ kswz(kr);
         b_kr[q] = kr;
         b_col[q] = min(n0 + c * 8, p.N - 8);
-        b_off[q] = (uint32_t)(((int64_t)kr * p.ldb + b_col[q]) * 2);
+        b_off[q] = (uint32_t)((((KRAG && p.b_gather) ? 0 : (int64_t)kr * p.ldb) + b_col[q]) * 2);
       }
     }
 
@@ -414,6 +416,14 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
       const uint32_t lds_b = ring_lds + NS * (BM * BK * 2) + slot * (BN * BK * 2) + wave_u * (LB * 1024);
       if constexpr (!A_KO) {
         dma_saddr<LA>(lds_a, uniform_ptr(a_base + kt * BK), a_off);
+      } else if ((kt + 1) * BK <= Kg) {
+        // full ragged-K stage: every k-row exists
+        uint32_t voff[LA];
+#pragma unroll
+        for (int q = 0; q < LA; ++q)
+          voff[q] = p.a_gather ? (uint32_t)ia[q] * (uint32_t)(p.lda * 2) + a_off[q] : a_off[q];
+        const uint16_t* base = p.a_gather ? p.A : p.A + (int64_t)(r0 + kt * BK) * p.lda;
+        dma_saddr<LA>(lds_a, uniform_ptr(base), voff);
       } else {
 #pragma unroll
         for (int q = 0; q < LA; ++q)
@@ -424,6 +434,13 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
         dma_saddr<LB>(lds_b, uniform_ptr(Bg + kt * BK), b_off);
       } else if constexpr (!KRAG) {
         dma_saddr<LB>(lds_b, uniform_ptr(Bg + (int64_t)kt * BK * p.ldb), b_off);
+      } else if ((kt + 1) * BK <= Kg) {
+        uint32_t voff[LB];
+#pragma unroll
+        for (int q = 0; q < LB; ++q)
+          voff[q] = p.b_gather ? (uint32_t)ib[q] * (uint32_t)(p.ldb * 2) + b_off[q] : b_off[q];
+        const uint16_t* base = p.b_gather ? p.B : p.B + (int64_t)(r0 + kt * BK) * p.ldb;
+        dma_saddr<LB>(lds_b, uniform_ptr(base), voff);
       } else {
 #pragma unroll
         for (int q = 0; q < LB; ++q)
@@ -510,8 +527,8 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
     // and stores are 16 bytes wide. acc[i][j][v] holds row i*32 + 8*(v/4) + 4*(lane/32) +
     // v%4 and column j*32 + lane%32 of the wavefront's block.
     if constexpr (EPI == EPI_F32) {
-      // fp32 weight gradients: 32 lanes already write 128 contiguous bytes of a row, so the
-      // accumulators go straight to memory.
+      // fp32 weight gradients: the 32 lanes of a half-wave write 128 contiguous bytes of a row
+      // (one full cache line) per store, so the accumulators go straight to memory.
       float* Cg = p.of + (int64_t)g * p.f_gstride;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
