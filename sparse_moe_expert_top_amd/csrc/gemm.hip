@@ -38,6 +38,8 @@
 //    gradients write fp32 rows (zeros for experts without rows).
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 #include "situ_math.h"
@@ -574,9 +576,15 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
             for (int q = 0; q < 4; ++q) {
               hg[q] = pack_bf16x2(gv[2 * q], gv[2 * q + 1]);
               hl[q] = pack_bf16x2(lv[2 * q], lv[2 * q + 1]);
-              av[q] = pack_bf16x2(situ_fwd(bf16_lo(hg[q]), bf16_lo(hl[q]), p.sc),
-                                  situ_fwd(bf16_hi(hg[q]), bf16_hi(hl[q]), p.sc));
             }
+            auto act = [&](auto b4) {
+              constexpr bool B4 = decltype(b4)::value;
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                av[q] = pack_bf16x2(situ_fwd<B4>(bf16_lo(hg[q]), bf16_lo(hl[q]), p.sc),
+                                    situ_fwd<B4>(bf16_hi(hg[q]), bf16_hi(hl[q]), p.sc));
+            };
+            if (p.sc.b4) act(std::true_type{}); else act(std::false_type{});
             *(u32x4*)&p.o0[r * p.ld0 + jj] = hg;
             *(u32x4*)&p.o0[r * p.ld0 + p.H + jj] = hl;
             *(u32x4*)&p.o1[r * p.ld1 + jj] = av;
@@ -612,18 +620,23 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
               const u32x4 hl = *(const u32x4*)&hr[p.H + col];
               u32x4 og, ol, oa;
               float acc_p = 0.0f;
+              auto grad = [&](auto b4) {
+                constexpr bool B4 = decltype(b4)::value;
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                float a0, dg0, dl0, a1, dg1, dl1;
-                situ_bwd(bf16_lo(hg[q]), bf16_lo(hl[q]), pr * cv[2 * q], p.sc, a0, dg0, dl0);
-                situ_bwd(bf16_hi(hg[q]), bf16_hi(hl[q]), pr * cv[2 * q + 1], p.sc, a1, dg1, dl1);
-                const float ab0 = round_bf16(a0), ab1 = round_bf16(a1);
-                acc_p += cv[2 * q] * ab0;
-                acc_p += cv[2 * q + 1] * ab1;
-                og[q] = pack_bf16x2(dg0, dg1);
-                ol[q] = pack_bf16x2(dl0, dl1);
-                oa[q] = pack_bf16x2(pr * ab0, pr * ab1);
-              }
+                for (int q = 0; q < 4; ++q) {
+                  float a0, dg0, dl0, a1, dg1, dl1;
+                  situ_bwd<B4>(bf16_lo(hg[q]), bf16_lo(hl[q]), pr * cv[2 * q], p.sc, a0, dg0, dl0);
+                  situ_bwd<B4>(bf16_hi(hg[q]), bf16_hi(hl[q]), pr * cv[2 * q + 1], p.sc, a1, dg1,
+                               dl1);
+                  const float ab0 = round_bf16(a0), ab1 = round_bf16(a1);
+                  acc_p += cv[2 * q] * ab0;
+                  acc_p += cv[2 * q + 1] * ab1;
+                  og[q] = pack_bf16x2(dg0, dg1);
+                  ol[q] = pack_bf16x2(dl0, dl1);
+                  oa[q] = pack_bf16x2(pr * ab0, pr * ab1);
+                }
+              };
+              if (p.sc.b4) grad(std::true_type{}); else grad(std::false_type{});
               uint16_t* dr = p.o0 + r * p.ld0;
               *(u32x4*)&dr[col] = og;
               *(u32x4*)&dr[p.H + col] = ol;

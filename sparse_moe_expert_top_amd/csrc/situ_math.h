@@ -6,21 +6,23 @@
 // The custom op of the same section keeps only the bf16 pre-activation and recomputes tanh
 // and sigmoid in the backward; this header is that recomputation.
 //
-// Evaluation (our own, chosen for gfx950's quarter-rate transcendental unit): every factor
-// is written with a decaying exponential of |x|, so nothing overflows and no NaN can come
-// from the tails:
+// Evaluation (our own, chosen for gfx950, where these kernels are bound by vector ALU
+// issue): every factor is written with a decaying exponential of |x|, so nothing overflows
+// and no NaN can come from the tails:
 //   e1 = exp(-2|g|/beta):  tanh(g/beta) = sgn(g) (1 - e1) / (1 + e1),
 //                          1 - tanh^2   = 4 e1 / (1 + e1)^2
 //   e2 = exp(-|g|):        sigmoid(g)   = (g >= 0 ? 1 : e2) / (1 + e2),
 //                          s (1 - s)    = e2 / (1 + e2)^2
 //   e3 = exp(-2|l|/lambda): tanh(l/lambda) = sgn(l) (1 - e3) / (1 + e3)
-// For tiny arguments 1 - e cancels, so 1 - exp(-y) switches to y (1 - y/2) when y < 2^-12
-// (the dropped y^3/6 term is below 2^-37 relative there); results that fall into fp32's
-// denormal range may flush to zero.
-// The forward folds the three denominators into one reciprocal (3 exp + 1 rcp). The
-// backward calls the same forward routine for `a`, so a recomputed activation is
-// bit-identical to the one the forward stored. Builds use -ffp-contract=off so the
-// compiler cannot fuse these operations differently in different callers.
+// With beta = 4 (the pages' default) e2 = e1^2, which saves one exponential (template flag
+// B4, chosen on the host from beta). For tiny arguments 1 - e cancels, so 1 - exp(-y) is
+// taken as y when y < 2^-12 (relative error below y/2 < 2^-13, far under bf16's spacing);
+// results in fp32's denormal range may flush to zero.
+// The forward folds its three denominators into one reciprocal; the backward takes one
+// reciprocal of their product and recovers the three from it. The backward calls the same
+// forward routine for `a`, so a recomputed activation is bit-identical to the one the
+// forward stored. Builds use -ffp-contract=off so the compiler cannot fuse these operations
+// differently in different callers.
 #pragma once
 
 #include "common.h"
@@ -36,6 +38,7 @@ struct SituCoef {
   float beta;
   float lam;
   float bl;      // beta * lambda
+  int b4;        // beta == 4: exp(-|g|) = exp(-|g|/2)^2
 };
 
 inline SituCoef make_situ_coef(float beta, float lam) {
@@ -49,6 +52,7 @@ inline SituCoef make_situ_coef(float beta, float lam) {
   c.beta = beta;
   c.lam = lam;
   c.bl = beta * lam;
+  c.b4 = (beta == 4.0f) ? 1 : 0;
   return c;
 }
 
@@ -57,15 +61,24 @@ __device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcp
 
 // 1 - exp(-y) for y >= 0, given e = exp(-y)
 __device__ __forceinline__ float one_minus_exp(float y, float e) {
-  return (y < 0x1p-12f) ? y * fmaf(-0.5f, y, 1.0f) : (1.0f - e);
+  return (y < 0x1p-12f) ? y : (1.0f - e);
+}
+
+// The three decaying exponentials of one (g, l) pair.
+template <bool B4>
+__device__ __forceinline__ void situ_exps(float ag, float al, const SituCoef& c, float& e1,
+                                          float& e2, float& e3) {
+  e1 = exp2_fast(-(ag * c.k1));
+  e2 = B4 ? e1 * e1 : exp2_fast(-(ag * c.k2));
+  e3 = exp2_fast(-(al * c.k3));
 }
 
 // a = gate'(g) * lin'(l)
+template <bool B4>
 __device__ __forceinline__ float situ_fwd(float g, float l, const SituCoef& c) {
   const float ag = fabsf(g), al = fabsf(l);
-  const float e1 = exp2_fast(-(ag * c.k1));
-  const float e2 = exp2_fast(-(ag * c.k2));
-  const float e3 = exp2_fast(-(al * c.k3));
+  float e1, e2, e3;
+  situ_exps<B4>(ag, al, c, e1, e2, e3);
   const float snum = (g >= 0.0f) ? 1.0f : e2;
   const float num = (one_minus_exp(ag * c.y1, e1) * snum) * one_minus_exp(al * c.y3, e3);
   const float den = ((1.0f + e1) * (1.0f + e2)) * (1.0f + e3);
@@ -75,17 +88,18 @@ __device__ __forceinline__ float situ_fwd(float g, float l, const SituCoef& c) {
   return __uint_as_float(__float_as_uint(mag) ^ sgn);
 }
 
-// Backward: returns a (bit-identical to situ_fwd), and dL/dg, dL/dl for upstream da.
-__device__ __forceinline__ void situ_bwd(float g, float l, float da, const SituCoef& c,
-                                         float& a, float& dg, float& dl) {
-  a = situ_fwd(g, l, c);
+// Backward: dL/dg, dL/dl for upstream da.
+template <bool B4>
+__device__ __forceinline__ void situ_grad(float g, float l, float da, const SituCoef& c,
+                                          float& dg, float& dl) {
   const float ag = fabsf(g), al = fabsf(l);
-  const float e1 = exp2_fast(-(ag * c.k1));
-  const float e2 = exp2_fast(-(ag * c.k2));
-  const float e3 = exp2_fast(-(al * c.k3));
-  const float r1 = rcp_fast(1.0f + e1);
-  const float r2 = rcp_fast(1.0f + e2);
-  const float r3 = rcp_fast(1.0f + e3);
+  float e1, e2, e3;
+  situ_exps<B4>(ag, al, c, e1, e2, e3);
+  const float p1 = 1.0f + e1, p2 = 1.0f + e2, p3 = 1.0f + e3;
+  const float p12 = p1 * p2;
+  const float rall = rcp_fast(p12 * p3);             // 1 / (p1 p2 p3)
+  const float r12 = rall * p3;                       // 1 / (p1 p2)
+  const float r1 = r12 * p2, r2 = r12 * p1, r3 = rall * p12;
   const float t1 = copysignf(one_minus_exp(ag * c.y1, e1) * r1, g);
   const float s = ((g >= 0.0f) ? 1.0f : e2) * r2;
   const float t2 = copysignf(one_minus_exp(al * c.y3, e3) * r3, l);
@@ -97,6 +111,14 @@ __device__ __forceinline__ void situ_bwd(float g, float l, float da, const SituC
   const float dgate = sech2_g * s + (c.beta * t1) * s1ms;
   dg = (da * lin) * dgate;
   dl = (da * gate) * sech2_l;
+}
+
+// Backward with the recomputed activation: a is bit-identical to situ_fwd<B4>(g, l, c).
+template <bool B4>
+__device__ __forceinline__ void situ_bwd(float g, float l, float da, const SituCoef& c,
+                                         float& a, float& dg, float& dl) {
+  a = situ_fwd<B4>(g, l, c);
+  situ_grad<B4>(g, l, da, c, dg, dl);
 }
 
 }  // namespace moe
