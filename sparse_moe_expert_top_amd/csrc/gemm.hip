@@ -10,8 +10,8 @@
 //   down      a[r] . w_down[e]^T              rows     d     H       rows         rows (NT)
 //   dA        dy[tok(r)] . w_down[e]          rows     H     d       rows+gather  k-outer (NN)
 //   dX        dh[r] . w_gu[e]                 rows     d     2H      rows         k-outer (NN)
-//   dW_down^T sum_r pa[r]^T dy[tok(r)]        H        d     rows    k-outer      k-outer+g (TN)
-//   dW_gu^T   sum_r x[tok(r)]^T dh[r]         d        2H    rows    k-outer+g    k-outer (TN)
+//   dW_down   sum_r dy[tok(r)]^T pa[r]        d        H     rows    k-outer+g    k-outer (TN)
+//   dW_gu     sum_r dh[r]^T x[tok(r)]         2H       d     rows    k-outer      k-outer+g (TN)
 //
 // Design (gfx950):
 //  * v_mfma_f32_32x32x16_bf16 with fp32 accumulators. A workgroup of WGM x WGN wavefronts
@@ -19,8 +19,12 @@
 //    configuration (256 x 256, 8 wavefronts, two per SIMD) loads 8 bytes per kFLOP.
 //  * K advances in stages of BK through an NS-slot LDS ring. Each stage is filled by
 //    direct-to-LDS loads (global_load_lds_dwordx4, 1 KiB per wavefront instruction), issued
-//    NS-1 stages ahead of its use; one barrier per stage orders fills after the reads of
-//    the slot they overwrite.
+//    NS-1 stages ahead of its use; one barrier per stage, placed before the stage's last
+//    k-step, orders fills after the reads of the slot they overwrite, and the last k-step's
+//    MFMAs cover the next stage's first fragment reads.
+//  * A wavefront whose 32-row fragments lie wholly past the end of a group's rows skips
+//    them (the k-loop is compiled once per count of live fragments), so the last, partly
+//    filled tile of each expert costs only the MFMAs of its live rows.
 //  * "rows" operands (K contiguous in HBM) stay [row][BK] in LDS, with an XOR swizzle of the
 //    16-byte chunks; each lane loads the chunk that belongs at its LDS position, optionally
 //    through a row index (the dispatch gather). MFMA fragments are ds_read_b128.
@@ -35,7 +39,7 @@
 //  * Epilogues: gate_up writes h (bf16) and a = bf16(SiTU-GLU(bf16 h)); down writes
 //    bf16(p * o) rows for the combine; dA recomputes a from the saved h, accumulates the
 //    per-row <G, a> partials, and writes dh and bf16(p a); dX writes bf16 rows; the weight
-//    gradients write fp32 rows (zeros for experts without rows).
+//    gradients write fp32 rows (zeros for experts without rows) with streaming stores.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -137,7 +141,16 @@ template <int L>
 __device__ __forceinline__ void dma_saddr(uint32_t lds0, const void* sbase,
                                           const uint32_t (&voff)[L]) {
   uint32_t saved;
-  if constexpr (L == 2) {
+  if constexpr (L == 1) {
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "global_load_lds_dwordx4 %3, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds0), "s"(sbase), "v"(voff[0])
+        : "memory");
+  } else if constexpr (L == 2) {
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
         "s_mov_b32 m0, %1\n\t"
@@ -190,6 +203,40 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i16x4 ds_read_tr(const uint16_t* lds_src) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) i16x4*)lds_src);
+}
+
+// Output stores of the epilogues; NT marks them streaming so they do not displace the
+// operand panels that neighbouring tiles re-read from L2.
+#ifndef MOE_NT_F32
+#define MOE_NT_F32 1
+#endif
+#ifndef MOE_NT_ROWS
+#define MOE_NT_ROWS 0
+#endif
+__device__ __forceinline__ void st_f32(float* p, float v) {
+#if MOE_NT_F32
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
+__device__ __forceinline__ void st_row16(uint16_t* p, u32x4 v) {
+#if MOE_NT_ROWS
+  __builtin_nontemporal_store(v, (u32x4*)p);
+#else
+  *(u32x4*)p = v;
+#endif
+}
+
+// Calls f(std::integral_constant<int, n>) for a runtime n in [0, N].
+template <int N, class F>
+__device__ __forceinline__ void dispatch_count(int n, F&& f) {
+  if constexpr (N == 0) {
+    f(std::integral_constant<int, 0>{});
+  } else {
+    if (n >= N) f(std::integral_constant<int, N>{});
+    else dispatch_count<N - 1>(n, f);
+  }
 }
 
 template <class C, bool KRAG, int BKIND, int EPI>
@@ -460,10 +507,14 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    auto load_frags = [&](int slot, int s, bf16x8 (&af)[FM], bf16x8 (&bfr)[FN]) {
+    // NF = fragments (32-row blocks) of this wave that hold rows of the group; the rest
+    // are neither read nor multiplied.
+    auto load_frags = [&](auto nfc, int slot, int s, bf16x8 (&af)[FM], bf16x8 (&bfr)[FN]) {
+      constexpr int NF = decltype(nfc)::value;
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        if constexpr (!A_KO) {
+        if (i >= NF) {
+        } else if constexpr (!A_KO) {
           af[i] = *(const bf16x8*)&sA[slot][abase[i] + astep[s][0]];
         } else {
           const i16x4 lo = ds_read_tr(&sA[slot][abase[i] + astep[s][0]]);
@@ -482,45 +533,72 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
         }
       }
     };
-    // Fragments of k-step s+1 are read while the MFMAs of step s run.
-    auto compute_stage = [&](int slot) {
-      bf16x8 fa[2][FM], fb[2][FN];
-      load_frags(slot, 0, fa[0], fb[0]);
+    auto mfma_step = [&](auto nfc, const bf16x8 (&af)[FM], const bf16x8 (&bfr)[FN]) {
+      constexpr int NF = decltype(nfc)::value;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        if (s + 1 < KS) load_frags(slot, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+      for (int i = 0; i < NF; ++i)
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][i], fb[s & 1][j],
-                                                                acc[i][j], 0, 0, 0);
-      }
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     };
-
-    // ------------------------------------------------------------ k pipeline
-    // Stages kt+1 .. kt+NS-2 stay in flight while stage kt is consumed. Before stage kt is
-    // read, this wave's loads for it have landed (vmcnt) and every wave's have (barrier);
-    // the same barrier orders the refill of the slot consumed in the previous iteration
-    // after every wave's reads of it.
-    fetch_rows(0);
-#pragma unroll
-    for (int st = 0; st < NS - 1; ++st)
-      if (st < nk) issue(st);
-    for (int kt = 0; kt < nk; ++kt) {
-      const int later = min(NS - 2, nk - 1 - kt);   // stages issued after kt
+    // Waits until this wave's loads of stage `next` have landed, `later` stages being issued
+    // after it, and until its own LDS reads are done.
+    auto wait_stage = [&](int later) {
       if (later >= 2) wait_vm_lgkm0<2 * (LPS + NIDX)>();
       else if (later == 1) wait_vm_lgkm0<LPS + NIDX>();
       else wait_vm_lgkm0<0>();
+    };
+
+    // ------------------------------------------------------------ k pipeline
+    // Stages kt+1 .. kt+NS-1 are in flight while stage kt is consumed. Fragments of k-step
+    // s+1 are read from LDS while the MFMAs of step s run. The barrier of stage kt sits
+    // before its last k-step: by then every wave has read all of stage kt into registers
+    // (so slot kt can be refilled with stage kt+NS) and has waited for its own loads of
+    // stage kt+1 (so after the barrier all of stage kt+1 is in LDS). The MFMAs of the last
+    // k-step then cover the refill's issue and the latency of stage kt+1's first fragment
+    // reads, instead of leaving the matrix core idle across the barrier.
+    static_assert(KS % 2 == 0, "fragment double buffer alternates within a stage");
+    auto kloop = [&](auto nfc) {
+      fetch_rows(0);
+#pragma unroll
+      for (int st = 0; st < NS - 1; ++st)
+        if (st < nk) issue(st);
+      wait_stage(min(NS - 2, nk - 1));
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      if (kt + NS - 1 < nk) issue(kt + NS - 1);
-      compute_stage(kt & (NS - 1));
+      if (NS - 1 < nk) issue(NS - 1);
+      bf16x8 fa[2][FM], fb[2][FN];
+      load_frags(nfc, 0, 0, fa[0], fb[0]);
+      for (int kt = 0; kt < nk; ++kt) {
+        const int slot = kt & (NS - 1);
+#pragma unroll
+        for (int s = 0; s + 1 < KS; ++s) {
+          load_frags(nfc, slot, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+          mfma_step(nfc, fa[s & 1], fb[s & 1]);
+        }
+        if (kt + 1 < nk) {
+          wait_stage(min(NS - 2, nk - 2 - kt));
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+          if (kt + NS < nk) issue(kt + NS);
+          load_frags(nfc, (kt + 1) & (NS - 1), 0, fa[0], fb[0]);
+        }
+        mfma_step(nfc, fa[1], fb[1]);
+      }
+      // every wave is done with the ring before the epilogue stages through it
+      wait_vm_lgkm0<0>();
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // Row GEMMs: a tile at the end of a group may hold only a few rows; this wave's
+    // fragments wholly past the group's last row are skipped (a wave-uniform count).
+    int nfv = FM;
+    if constexpr (!KRAG) {
+      const int wrow0 = m0 + (wave_u / C::WGN) * WM;
+      nfv = max(0, min(FM, (Mg - wrow0 + 31) / 32));
     }
-    // every wave is done with the ring before the next tile refills it
-    wait_vm_lgkm0<0>();
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
+    nfv = __builtin_amdgcn_readfirstlane(nfv);
+    dispatch_count<FM>(nfv, kloop);
 
     // ------------------------------------------------------------ epilogues
     // Each wavefront stages one 32-row block of its accumulators at a time in LDS (fp32,
@@ -540,7 +618,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int row = m0 + wm * WM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-            if (row < p.M && col < p.N) Cg[(int64_t)row * p.ldf + col] = acc[i][j][v];
+            if (row < p.M && col < p.N) st_f32(&Cg[(int64_t)row * p.ldf + col], acc[i][j][v]);
           }
         }
     } else {
@@ -550,6 +628,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
     float* st = reinterpret_cast<float*>(ring) + wave * 32 * EPS;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      if (i >= nfv) break;
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -585,9 +664,9 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
                                     situ_fwd<B4>(bf16_hi(hg[q]), bf16_hi(hl[q]), p.sc));
             };
             if (p.sc.b4) act(std::true_type{}); else act(std::false_type{});
-            *(u32x4*)&p.o0[r * p.ld0 + jj] = hg;
-            *(u32x4*)&p.o0[r * p.ld0 + p.H + jj] = hl;
-            *(u32x4*)&p.o1[r * p.ld1 + jj] = av;
+            st_row16(&p.o0[r * p.ld0 + jj], hg);
+            st_row16(&p.o0[r * p.ld0 + p.H + jj], hl);
+            st_row16(&p.o1[r * p.ld1 + jj], av);
           }
         }
       } else {
@@ -609,7 +688,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
               u32x4 o;
 #pragma unroll
               for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(cv[2 * q] * sc, cv[2 * q + 1] * sc);
-              *(u32x4*)&p.o0[r * p.ld0 + col] = o;
+              st_row16(&p.o0[r * p.ld0 + col], o);
             }
           } else if constexpr (EPI == EPI_DA) {
             if (rblk + row < Mg && col < p.N) {
@@ -638,9 +717,9 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
               };
               if (p.sc.b4) grad(std::true_type{}); else grad(std::false_type{});
               uint16_t* dr = p.o0 + r * p.ld0;
-              *(u32x4*)&dr[col] = og;
-              *(u32x4*)&dr[p.H + col] = ol;
-              *(u32x4*)&p.o1[r * p.ld1 + col] = oa;
+              st_row16(&dr[col], og);
+              st_row16(&dr[p.H + col], ol);
+              st_row16(&p.o1[r * p.ld1 + col], oa);
               part[ps] = acc_p;
             }
           }
@@ -694,7 +773,7 @@ static hipError_t run_gemm(const GemmArgs& args, int64_t max_tiles, hipStream_t 
 #define MOE_CFG_DN CfgBig
 #endif
 #ifndef MOE_CFG_DA
-#define MOE_CFG_DA CfgMid
+#define MOE_CFG_DA CfgBig
 #endif
 #ifndef MOE_CFG_DX
 #define MOE_CFG_DX CfgBig
