@@ -124,7 +124,8 @@ __device__ __attribute__((aligned(16))) uint16_t g_zero_row[256];
 // itself (explicit vmcnt waits plus barriers); M0 is saved and restored around them.
 //
 // dma_vaddr: one load from a per-lane 64-bit address.
-__device__ __forceinline__ void dma_vaddr(const uint16_t* src, uint32_t lds_addr) {
+__device__ __forceinline__ void dma_vaddr(const uint16_t* src, uint32_t lds_in) {
+  const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(lds_in);
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -138,8 +139,9 @@ __device__ __forceinline__ void dma_vaddr(const uint16_t* src, uint32_t lds_addr
 // dma_saddr: L loads from a wave-uniform 64-bit base plus per-lane 32-bit byte offsets;
 // load q lands at lds0 + 1024 q.
 template <int L>
-__device__ __forceinline__ void dma_saddr(uint32_t lds0, const void* sbase,
+__device__ __forceinline__ void dma_saddr(uint32_t lds0_in, const void* sbase,
                                           const uint32_t (&voff)[L]) {
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds0_in);
   uint32_t saved;
   if constexpr (L == 1) {
     asm volatile(
@@ -161,6 +163,13 @@ __device__ __forceinline__ void dma_saddr(uint32_t lds0, const void* sbase,
         : "=&s"(saved)
         : "s"(lds0), "s"(lds0 + 1024u), "s"(sbase), "v"(voff[0]), "v"(voff[1])
         : "memory");
+  } else if constexpr (L > 4) {
+    static_assert(L % 4 == 0, "loads per operand per stage");
+#pragma unroll
+    for (int h = 0; h < L / 4; ++h) {
+      const uint32_t part[4] = {voff[4 * h], voff[4 * h + 1], voff[4 * h + 2], voff[4 * h + 3]};
+      dma_saddr<4>(lds0 + 4096u * h, sbase, part);
+    }
   } else {
     static_assert(L == 4, "loads per operand per stage");
     asm volatile(
@@ -249,7 +258,6 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
   constexpr int LA = BM * BK * 2 / 1024 / NW;       // direct-to-LDS loads per wave per stage
   constexpr int LB = BN * BK * 2 / 1024 / NW;
   constexpr int LPS = LA + LB;
-  constexpr int NIDX = KRAG ? LPS : 0;              // gather-index loads per wave per stage
   constexpr int KS = BK / 16;                       // MFMA k-steps per stage
   constexpr int GPT = (1024 + NT - 1) / NT;         // expert offsets per thread in the scan
   static_assert(LA * 1024 * NW == BM * BK * 2 && LB * 1024 * NW == BN * BK * 2, "loads");
@@ -313,7 +321,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
 
   // GROUP_M rasterization of a tile inside its expert: super-rows of group_m m-tiles, each
   // swept over all n-tiles with the m index fastest.
-  auto raster = [&](int local, int mtiles, int &mt, int &nt) {
+  auto raster = [&](int local, int mtiles, int &mt, int &nt) __attribute__((always_inline)) {
     const int gm = p.group_m;
     const int per_super = gm * p.n_tiles;
     const int sr = local / per_super;
@@ -442,24 +450,31 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
       }
     }
 
-    // Ragged-K operands: storage row of each load's k-row for the next stage to issue
-    // (-1 past the group's end), fetched one stage ahead of its use.
-    int ia[KRAG ? LA : 1], ib[KRAG ? LB : 1];
-    auto fetch_rows = [&](int kt) {
+    // Ragged-K operands. In a full stage this wave's loads cover KPW consecutive k-rows;
+    // their storage rows (for a gathered operand) come from one scalar load, issued one
+    // stage ahead. Scalar loads are counted by lgkmcnt, so using them never waits for the
+    // direct-to-LDS loads in flight (per-lane index loads would: vmcnt retires in order).
+    // The partial last stage looks its rows up per lane when it is issued.
+    constexpr int KPW = BK / NW;
+    static_assert(!KRAG || (BM == 256 && BN == 256 && KPW == 2 * LA && KPW == 2 * LB),
+                  "a full-stage load covers two k-rows, one per half-wave");
+    typedef int kidx_t __attribute__((ext_vector_type(KPW)));
+    typedef __attribute__((address_space(4))) const kidx_t cidx_t;
+    kidx_t ga{}, gb{};
+    auto fetch_rows = [&](int kt) __attribute__((always_inline)) {
       if constexpr (KRAG) {
-#pragma unroll
-        for (int q = 0; q < LA; ++q) {
-          const int kg = kt * BK + a_kr[q];
-          ia[q] = (kg < Kg) ? (p.a_gather ? p.a_gather[r0 + kg] : (r0 + kg)) : -1;
-        }
-#pragma unroll
-        for (int q = 0; q < LB; ++q) {
-          const int kg = kt * BK + b_kr[q];
-          ib[q] = (kg < Kg) ? (p.b_gather ? p.b_gather[r0 + kg] : (r0 + kg)) : -1;
+        if ((kt + 1) * BK <= Kg) {
+          const int k0 = r0 + kt * BK + wave_u * KPW;
+          if (p.a_gather) ga = *(cidx_t*)(p.a_gather + k0);
+          if (p.b_gather) gb = *(cidx_t*)(p.b_gather + k0);
         }
       }
     };
-    auto issue = [&](int kt) {
+    auto tail_row = [&](const int32_t* gather, int kr) __attribute__((always_inline)) {
+      const int kg = kr;
+      return (kg < Kg) ? (gather ? gather[r0 + kg] : (r0 + kg)) : -1;
+    };
+    auto issue = [&](int kt) __attribute__((always_inline)) {
       const int slot = kt & (NS - 1);
       const uint32_t lds_a = ring_lds + slot * (BM * BK * 2) + wave_u * (LA * 1024);
       const uint32_t lds_b = ring_lds + NS * (BM * BK * 2) + slot * (BN * BK * 2) + wave_u * (LB * 1024);
@@ -470,14 +485,18 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
         uint32_t voff[LA];
 #pragma unroll
         for (int q = 0; q < LA; ++q)
-          voff[q] = p.a_gather ? (uint32_t)ia[q] * (uint32_t)(p.lda * 2) + a_off[q] : a_off[q];
+          voff[q] = p.a_gather ? (uint32_t)(lane < 32 ? ga[2 * q] : ga[2 * q + 1]) *
+                                         (uint32_t)(p.lda * 2) + a_off[q]
+                               : a_off[q];
         const uint16_t* base = p.a_gather ? p.A : p.A + (int64_t)(r0 + kt * BK) * p.lda;
         dma_saddr<LA>(lds_a, uniform_ptr(base), voff);
       } else {
 #pragma unroll
-        for (int q = 0; q < LA; ++q)
-          dma_vaddr((ia[q] >= 0) ? p.A + (int64_t)ia[q] * p.lda + a_col[q] : g_zero_row,
+        for (int q = 0; q < LA; ++q) {
+          const int ra = tail_row(p.a_gather, kt * BK + a_kr[q]);
+          dma_vaddr((ra >= 0) ? p.A + (int64_t)ra * p.lda + a_col[q] : g_zero_row,
                     lds_a + q * 1024);
+        }
       }
       if constexpr (!B_KO) {
         dma_saddr<LB>(lds_b, uniform_ptr(Bg + kt * BK), b_off);
@@ -487,14 +506,18 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
         uint32_t voff[LB];
 #pragma unroll
         for (int q = 0; q < LB; ++q)
-          voff[q] = p.b_gather ? (uint32_t)ib[q] * (uint32_t)(p.ldb * 2) + b_off[q] : b_off[q];
+          voff[q] = p.b_gather ? (uint32_t)(lane < 32 ? gb[2 * q] : gb[2 * q + 1]) *
+                                         (uint32_t)(p.ldb * 2) + b_off[q]
+                               : b_off[q];
         const uint16_t* base = p.b_gather ? p.B : p.B + (int64_t)(r0 + kt * BK) * p.ldb;
         dma_saddr<LB>(lds_b, uniform_ptr(base), voff);
       } else {
 #pragma unroll
-        for (int q = 0; q < LB; ++q)
-          dma_vaddr((ib[q] >= 0) ? p.B + (int64_t)ib[q] * p.ldb + b_col[q] : g_zero_row,
+        for (int q = 0; q < LB; ++q) {
+          const int rb = tail_row(p.b_gather, kt * BK + b_kr[q]);
+          dma_vaddr((rb >= 0) ? p.B + (int64_t)rb * p.ldb + b_col[q] : g_zero_row,
                     lds_b + q * 1024);
+        }
       }
       if (kt + 1 < nk) fetch_rows(kt + 1);
     };
@@ -509,7 +532,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
 
     // NF = fragments (32-row blocks) of this wave that hold rows of the group; the rest
     // are neither read nor multiplied.
-    auto load_frags = [&](auto nfc, int slot, int s, bf16x8 (&af)[FM], bf16x8 (&bfr)[FN]) {
+    auto load_frags = [&](auto nfc, int slot, int s, bf16x8 (&af)[FM], bf16x8 (&bfr)[FN]) __attribute__((always_inline)) {
       constexpr int NF = decltype(nfc)::value;
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
@@ -533,7 +556,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
         }
       }
     };
-    auto mfma_step = [&](auto nfc, const bf16x8 (&af)[FM], const bf16x8 (&bfr)[FN]) {
+    auto mfma_step = [&](auto nfc, const bf16x8 (&af)[FM], const bf16x8 (&bfr)[FN]) __attribute__((always_inline)) {
       constexpr int NF = decltype(nfc)::value;
 #pragma unroll
       for (int i = 0; i < NF; ++i)
@@ -543,9 +566,9 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
     };
     // Waits until this wave's loads of stage `next` have landed, `later` stages being issued
     // after it, and until its own LDS reads are done.
-    auto wait_stage = [&](int later) {
-      if (later >= 2) wait_vm_lgkm0<2 * (LPS + NIDX)>();
-      else if (later == 1) wait_vm_lgkm0<LPS + NIDX>();
+    auto wait_stage = [&](int later) __attribute__((always_inline)) {
+      if (later >= 2) wait_vm_lgkm0<2 * LPS>();
+      else if (later == 1) wait_vm_lgkm0<LPS>();
       else wait_vm_lgkm0<0>();
     };
 
@@ -558,7 +581,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
     // k-step then cover the refill's issue and the latency of stage kt+1's first fragment
     // reads, instead of leaving the matrix core idle across the barrier.
     static_assert(KS % 2 == 0, "fragment double buffer alternates within a stage");
-    auto kloop = [&](auto nfc) {
+    auto kloop = [&](auto nfc) __attribute__((always_inline)) {
       fetch_rows(0);
 #pragma unroll
       for (int st = 0; st < NS - 1; ++st)
@@ -598,7 +621,8 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
       nfv = max(0, min(FM, (Mg - wrow0 + 31) / 32));
     }
     nfv = __builtin_amdgcn_readfirstlane(nfv);
-    dispatch_count<FM>(nfv, kloop);
+    if constexpr (KRAG) kloop(std::integral_constant<int, FM>{});
+    else dispatch_count<FM>(nfv, kloop);
 
     // ------------------------------------------------------------ epilogues
     // Each wavefront stages one 32-row block of its accumulators at a time in LDS (fp32,
