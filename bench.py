@@ -24,6 +24,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE expert fwd+bwd TFLOP/s (% bf16 MFMA peak); SiTU-GLU GB/s (% HBM)"
+# HBM counters of the gate/up GEMM on the shard workload, taken with rocprofv3 (FETCH_SIZE and
+# WRITE_SIZE passes over `bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-situ`, scaled by
+# the same counters over `bench.py --calibrate-copy`). They describe the kernel sources whose
+# digest they record; for any other sources `traffic` is null.
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "gate_up_shard_counters.md")
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
@@ -37,7 +42,58 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-situ", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run 3 plain 1 GiB device copies (counter calibration)")
+    ap.add_argument("--print-digest", action="store_true",
+                    help="print the digest of the kernel sources and exit")
     return ap.parse_args()
+
+
+def kernel_source_digest():
+    """sha256 over the HIP sources and the build flags of the library."""
+    import hashlib
+    pkg = os.path.join(ROOT, "sparse_moe_expert_top_amd")
+    h = hashlib.sha256()
+    files = [os.path.join(pkg, "csrc", f) for f in sorted(os.listdir(os.path.join(pkg, "csrc")))]
+    for f in files + [os.path.join(pkg, "build.py")]:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def committed_traffic(workload):
+    """HBM bytes per gate/up launch from the committed counter summary, or None when the
+    summary is missing, is for another workload, or was taken on other kernel sources."""
+    if workload != "shard" or not os.path.exists(COUNTERS_FILE):
+        return None
+    kv = {}
+    with open(COUNTERS_FILE) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith(("#", "|", " ", "`")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return {"fetch": float(kv["fetch_bytes_per_launch"]),
+                "write": float(kv["write_bytes_per_launch"])}
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy():
+    """Three plain device copies of 1 GiB: FETCH_SIZE / WRITE_SIZE of these dispatches give
+    the counters' scale (bytes per counted KiB)."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
+                      "dispatches": 3}), flush=True)
 
 
 def bf16_dev(u16, torch):
@@ -92,6 +148,12 @@ def main():
         print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE "
               f"{world}); this layer is measured on one GPU's share of experts", file=sys.stderr)
         sys.exit(2)
+    if args.print_digest:
+        print(kernel_source_digest())
+        return
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
 
     import torch
     import sparse_moe_expert_top_amd as moe
@@ -158,6 +220,9 @@ def main():
                   down_combine=evs[2].elapsed_time(evs[3]), backward=evs[3].elapsed_time(evs[4]))
     peak_gb = torch.cuda.max_memory_allocated() / 1e9
 
+    # gate/up moves each local expert's [2H, d] weights once, the R gathered rows of x, and
+    # writes h [R, 2H] and a [R, H]
+    gu_bytes = 2.0 * (cfg.E_loc * 2 * cfg.H * cfg.d + R * cfg.d + R * 3 * cfg.H)
     value = flop_step / (ms_step * 1e-3) / 1e12
     gu_tflops = flop_gu / (gu_ms * 1e-3) / 1e12
     out = {
@@ -173,12 +238,17 @@ def main():
                      "achieved": round(gu_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4),
                      "avg_launch_ms": round(gu_ms, 4), "flop_per_launch": flop_gu,
-                     "traffic": None},
+                     "algorithmic_bytes_per_launch": gu_bytes, "traffic": None},
         "phase_ms": {k: round(v, 4) for k, v in phases.items()},
         "peak_hbm_GB": round(peak_gb, 2),
         "saved_activation_GB": round((R * 2 * cfg.H * 2 + cfg.T * cfg.d * 2) / 1e9, 3),
         "naive_saved_fp32_GB": round(6 * R * cfg.H * 4 / 1e9, 3),
     }
+    tr = committed_traffic(args.workload)
+    if tr is not None:
+        out["roofline"]["traffic"] = tr["fetch"] + tr["write"]
+        out["roofline"].update(traffic_fetch_bytes=tr["fetch"], traffic_write_bytes=tr["write"],
+                               traffic_vs_algorithmic=round((tr["fetch"] + tr["write"]) / gu_bytes, 3))
     del buf
     torch.cuda.empty_cache()
 
