@@ -237,6 +237,26 @@ __device__ __forceinline__ void st_row16(uint16_t* p, u32x4 v) {
 #endif
 }
 
+// Workgroup barrier that the compiler may not move LDS or global accesses across (the
+// builtin alone is not a memory operation for it); emits only s_barrier.
+__device__ __forceinline__ void block_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, fully unrolled.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for_impl(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_impl<I + 1, N>(f);
+  }
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) { static_for_impl<0, N>(f); }
+
 // Calls f(std::integral_constant<int, n>) for a runtime n in [0, N].
 template <int N, class F>
 __device__ __forceinline__ void dispatch_count(int n, F&& f) {
@@ -404,8 +424,17 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
     // Rows and fixed-K k-outer operands: wave-uniform base (advanced per stage) plus a
     // per-lane 32-bit byte offset. Ragged-K k-outer operands: k-row and column per load.
     uint32_t a_off[LA], b_off[LB];
-    int a_kr[LA], a_col[LA];
-    int b_kr[LB], b_col[LB];
+    // k-row and column of load q of a k-outer operand with TR columns per k-row (recomputed
+    // where needed: only the partial last stage of a ragged-K tile uses them per lane)
+    auto kout_kr = [&](int q, int L, int TR) __attribute__((always_inline)) {
+      return ((wave * L + q) * 1024 + lane * 16) / (TR * 2);
+    };
+    auto kout_col = [&](int q, int L, int TR, int t0, int ext) __attribute__((always_inline)) {
+      const int byte = (wave * L + q) * 1024 + lane * 16;
+      const int kr = byte / (TR * 2);
+      const int c = ((byte % (TR * 2)) >> 4) ^ kswz(kr);
+      return min(t0 + c * 8, ext - 8);
+    };
     // rows of A: gathered rows are addressed from A itself, contiguous rows from row r0
     const uint16_t* a_base = p.a_gather ? p.A : p.A + (int64_t)r0 * p.lda;
 #pragma unroll
@@ -420,10 +449,9 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
       } else {
         const int kr = byte / (BM * 2);
         const int c = ((byte % (BM * 2)) >> 4) ^ kswz(kr);
-        a_kr[q] = kr;
-        a_col[q] = min(m0 + c * 8, p.M - 8);
+        const int a_col = min(m0 + c * 8, p.M - 8);
         // full stages: gathered rows add idx * lda at issue; contiguous rows are fixed here
-        a_off[q] = (uint32_t)(((p.a_gather ? 0 : (int64_t)kr * p.lda) + a_col[q]) * 2);
+        a_off[q] = (uint32_t)(((p.a_gather ? 0 : (int64_t)kr * p.lda) + a_col) * 2);
       }
     }
 #pragma unroll
@@ -444,9 +472,8 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
       } else {
         const int kr = byte / (BN * 2);
         const int c = ((byte % (BN * 2)) >> 4) ^ kswz(kr);
-        b_kr[q] = kr;
-        b_col[q] = min(n0 + c * 8, p.N - 8);
-        b_off[q] = (uint32_t)((((KRAG && p.b_gather) ? 0 : (int64_t)kr * p.ldb) + b_col[q]) * 2);
+        const int b_col = min(n0 + c * 8, p.N - 8);
+        b_off[q] = (uint32_t)((((KRAG && p.b_gather) ? 0 : (int64_t)kr * p.ldb) + b_col) * 2);
       }
     }
 
@@ -461,23 +488,26 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
     typedef int kidx_t __attribute__((ext_vector_type(KPW)));
     typedef __attribute__((address_space(4))) const kidx_t cidx_t;
     kidx_t ga{}, gb{};
-    auto fetch_rows = [&](int kt) __attribute__((always_inline)) {
+    auto fetch_a = [&](int kt) __attribute__((always_inline)) {
       if constexpr (KRAG) {
-        if ((kt + 1) * BK <= Kg) {
-          const int k0 = r0 + kt * BK + wave_u * KPW;
-          if (p.a_gather) ga = *(cidx_t*)(p.a_gather + k0);
-          if (p.b_gather) gb = *(cidx_t*)(p.b_gather + k0);
-        }
+        if ((kt + 1) * BK <= Kg && p.a_gather)
+          ga = *(cidx_t*)(p.a_gather + r0 + kt * BK + wave_u * KPW);
+      }
+    };
+    auto fetch_b = [&](int kt) __attribute__((always_inline)) {
+      if constexpr (KRAG) {
+        if ((kt + 1) * BK <= Kg && p.b_gather)
+          gb = *(cidx_t*)(p.b_gather + r0 + kt * BK + wave_u * KPW);
       }
     };
     auto tail_row = [&](const int32_t* gather, int kr) __attribute__((always_inline)) {
       const int kg = kr;
       return (kg < Kg) ? (gather ? gather[r0 + kg] : (r0 + kg)) : -1;
     };
-    auto issue = [&](int kt) __attribute__((always_inline)) {
+    // A operand of stage kt: direct-to-LDS loads.
+    auto issue_a = [&](int kt) __attribute__((always_inline)) {
       const int slot = kt & (NS - 1);
       const uint32_t lds_a = ring_lds + slot * (BM * BK * 2) + wave_u * (LA * 1024);
-      const uint32_t lds_b = ring_lds + NS * (BM * BK * 2) + slot * (BN * BK * 2) + wave_u * (LB * 1024);
       if constexpr (!A_KO) {
         dma_saddr<LA>(lds_a, uniform_ptr(a_base + kt * BK), a_off);
       } else if ((kt + 1) * BK <= Kg) {
@@ -493,33 +523,52 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
       } else {
 #pragma unroll
         for (int q = 0; q < LA; ++q) {
-          const int ra = tail_row(p.a_gather, kt * BK + a_kr[q]);
-          dma_vaddr((ra >= 0) ? p.A + (int64_t)ra * p.lda + a_col[q] : g_zero_row,
+          const int ra = tail_row(p.a_gather, kt * BK + kout_kr(q, LA, BM));
+          dma_vaddr((ra >= 0) ? p.A + (int64_t)ra * p.lda + kout_col(q, LA, BM, m0, p.M) : g_zero_row,
                     lds_a + q * 1024);
         }
       }
-      if constexpr (!B_KO) {
-        dma_saddr<LB>(lds_b, uniform_ptr(Bg + kt * BK), b_off);
-      } else if constexpr (!KRAG) {
-        dma_saddr<LB>(lds_b, uniform_ptr(Bg + (int64_t)kt * BK * p.ldb), b_off);
-      } else if ((kt + 1) * BK <= Kg) {
+      if (kt + 1 < nk) fetch_a(kt + 1);
+    };
+    // B operand of stage kt: wave-uniform base and per-lane byte offsets (full stages), or
+    // the per-lane source row (partial ragged-K stage; nullptr reads as zeros).
+    auto b_base = [&](int kt) __attribute__((always_inline)) -> const uint16_t* {
+      if constexpr (!B_KO) return Bg + kt * BK;
+      else if constexpr (!KRAG) return Bg + (int64_t)kt * BK * p.ldb;
+      else return p.b_gather ? p.B : p.B + (int64_t)(r0 + kt * BK) * p.ldb;
+    };
+    auto b_voff = [&](int q) __attribute__((always_inline)) -> uint32_t {
+      if constexpr (KRAG)
+        return p.b_gather ? (uint32_t)(lane < 32 ? gb[2 * q] : gb[2 * q + 1]) *
+                                    (uint32_t)(p.ldb * 2) + b_off[q]
+                          : b_off[q];
+      else return b_off[q];
+    };
+    auto b_full = [&](int kt) __attribute__((always_inline)) {
+      return !KRAG || (kt + 1) * BK <= Kg;
+    };
+    // B operand, direct-to-LDS form.
+    auto issue_b = [&](int kt) __attribute__((always_inline)) {
+      const int slot = kt & (NS - 1);
+      const uint32_t lds_b = ring_lds + NS * (BM * BK * 2) + slot * (BN * BK * 2) + wave_u * (LB * 1024);
+      if (b_full(kt)) {
         uint32_t voff[LB];
 #pragma unroll
-        for (int q = 0; q < LB; ++q)
-          voff[q] = p.b_gather ? (uint32_t)(lane < 32 ? gb[2 * q] : gb[2 * q + 1]) *
-                                         (uint32_t)(p.ldb * 2) + b_off[q]
-                               : b_off[q];
-        const uint16_t* base = p.b_gather ? p.B : p.B + (int64_t)(r0 + kt * BK) * p.ldb;
-        dma_saddr<LB>(lds_b, uniform_ptr(base), voff);
+        for (int q = 0; q < LB; ++q) voff[q] = b_voff(q);
+        dma_saddr<LB>(lds_b, uniform_ptr(b_base(kt)), voff);
       } else {
 #pragma unroll
         for (int q = 0; q < LB; ++q) {
-          const int rb = tail_row(p.b_gather, kt * BK + b_kr[q]);
-          dma_vaddr((rb >= 0) ? p.B + (int64_t)rb * p.ldb + b_col[q] : g_zero_row,
+          const int rb = tail_row(p.b_gather, kt * BK + kout_kr(q, LB, BN));
+          dma_vaddr((rb >= 0) ? p.B + (int64_t)rb * p.ldb + kout_col(q, LB, BN, n0, p.N) : g_zero_row,
                     lds_b + q * 1024);
         }
       }
-      if (kt + 1 < nk) fetch_rows(kt + 1);
+      if (kt + 1 < nk) fetch_b(kt + 1);
+    };
+    auto issue = [&](int kt) __attribute__((always_inline)) {
+      issue_a(kt);
+      issue_b(kt);
     };
 
     f32x16 acc[FM][FN];
@@ -582,15 +631,15 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
     // reads, instead of leaving the matrix core idle across the barrier.
     static_assert(KS % 2 == 0, "fragment double buffer alternates within a stage");
     auto kloop = [&](auto nfc) __attribute__((always_inline)) {
-      fetch_rows(0);
+      bf16x8 fa[2][FM], fb[2][FN];
+      fetch_a(0);
+      fetch_b(0);
 #pragma unroll
       for (int st = 0; st < NS - 1; ++st)
         if (st < nk) issue(st);
       wait_stage(min(NS - 2, nk - 1));
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
+      block_sync();
       if (NS - 1 < nk) issue(NS - 1);
-      bf16x8 fa[2][FM], fb[2][FN];
       load_frags(nfc, 0, 0, fa[0], fb[0]);
       for (int kt = 0; kt < nk; ++kt) {
         const int slot = kt & (NS - 1);
@@ -601,8 +650,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
         }
         if (kt + 1 < nk) {
           wait_stage(min(NS - 2, nk - 2 - kt));
-          __builtin_amdgcn_s_barrier();
-          __builtin_amdgcn_sched_barrier(0);
+          block_sync();
           if (kt + NS < nk) issue(kt + NS);
           load_frags(nfc, (kt + 1) & (NS - 1), 0, fa[0], fb[0]);
         }
@@ -610,8 +658,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
       }
       // every wave is done with the ring before the epilogue stages through it
       wait_vm_lgkm0<0>();
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
+      block_sync();
     };
     // Row GEMMs: a tile at the end of a group may hold only a few rows; this wave's
     // fragments wholly past the group's last row are skipped (a wave-uniform count).
@@ -766,8 +813,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
     }
     // the next tile refills the ring only after every wave has read its staging
     wait_vm_lgkm0<0>();
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
+    block_sync();
   }
 }
 
