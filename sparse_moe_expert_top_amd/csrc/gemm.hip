@@ -681,17 +681,39 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
       // fp32 weight gradients: the 32 lanes of a half-wave write 128 contiguous bytes of a row
       // (one full cache line) per store, so the accumulators go straight to memory.
       float* Cg = p.of + (int64_t)g * p.f_gstride;
+      if (m0 + BM <= p.M && n0 + BN <= p.N) {
+        // Whole tile in range: a per-lane 32-bit byte offset from the tile origin plus a
+        // wave-uniform offset per store (no per-store guard or 64-bit multiply; an expert's
+        // block of the output is well under 4 GiB). The offsets are laundered through empty
+        // asm each tile so the compiler recomputes them here instead of keeping all 128 live.
+        char* Ct = reinterpret_cast<char*>(Cg + (int64_t)m0 * p.ldf + n0);
+        uint32_t ld4 = (uint32_t)p.ldf * 4u;
+        uint32_t lo4 = ((uint32_t)(wm * WM + (lane >> 5) * 4) * (uint32_t)p.ldf +
+                        (uint32_t)(wn * WN + (lane & 31))) * 4u;
+        asm volatile("" : "+s"(ld4));
+        asm volatile("" : "+v"(lo4));
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = n0 + wn * WN + j * 32 + (lane & 31);
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int row = m0 + wm * WM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-            if (row < p.M && col < p.N) st_f32(&Cg[(int64_t)row * p.ldf + col], acc[i][j][v]);
+            const uint32_t o = lo4 + (uint32_t)(i * 32 + (v >> 2) * 8 + (v & 3)) * ld4;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+              st_f32(reinterpret_cast<float*>(Ct + o + (uint32_t)(j * 128)), acc[i][j][v]);
           }
-        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int col = n0 + wn * WN + j * 32 + (lane & 31);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int row = m0 + wm * WM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+              if (row < p.M && col < p.N) st_f32(&Cg[(int64_t)row * p.ldf + col], acc[i][j][v]);
+            }
+          }
+      }
     } else {
     constexpr int EPS = WN + 8;
     static_assert(WN == 64, "epilogue lane mapping assumes 64-column wavefront blocks");
