@@ -12,62 +12,123 @@
 namespace moe {
 
 // ------------------------------------------------------------------------------ routing
-// One wavefront per token. Each lane holds NV logits (expert e = lane + 64 i). k rounds of
-// a wavefront arg-max (value descending, index ascending on ties) pick the slots in order;
-// the picked value's owner lane retires it. The softmax runs in fp32 over the k picks.
+// One wavefront per token; lane l holds the logits of experts l, l+64, ... . Every logit
+// becomes a 64-bit key whose order is the routing order: the high word is the fp32 value
+// mapped to an unsigned order (after -0 -> +0, so the two zeros tie), the low word is the
+// complement of the expert index (equal values: lower index first). Keys are unique, so
+// "the k largest keys in descending order" is exactly the slot order.
+//
+// Selection: thr = the k-th largest of the 64 per-lane maxima, taken over the keys' value
+// words by a bitwise radix select (one ballot per bit). At least k logits have a value at
+// or above thr, so the top k are among them. When at most 64 pass (the usual case: ~20-30
+// of 896 for k = 16), they are compacted through LDS, each one's rank among them is counted
+// from broadcast LDS reads, and the k best are placed by rank; lane j then holds slot j.
+// Otherwise (many ties) k rounds of a wave arg-max pick them one by one. The softmax runs
+// in fp32 over the k picked values.
+__device__ __forceinline__ uint64_t route_key(float v, int e) {
+  const uint32_t b = __float_as_uint(v + 0.0f);
+  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)(~e);
+}
+__device__ __forceinline__ float key_value(uint64_t k) {
+  const uint32_t o = (uint32_t)(k >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+__device__ __forceinline__ int key_index(uint64_t k) { return (int)~(uint32_t)k; }
+
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m, 64);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const uint64_t o = shfl_xor64(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
 template <int NV>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
                                                          int64_t T, int E, int k,
                                                          int32_t* __restrict__ idx_out,
                                                          float* __restrict__ gates_out) {
+  __shared__ uint64_t cand[4][64];
+  __shared__ uint64_t sel[4][32];
   const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
   const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int64_t nwave = ((int64_t)gridDim.x * blockDim.x) >> 6;
   for (int64_t t = wave; t < T; t += nwave) {
     const float* row = logits + t * (int64_t)E;
-    float v[NV];
-    uint32_t retired = 0;
+    uint64_t key[NV];
+    uint32_t lmax = 0;                                // value word of the lane's best key
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int e = lane + 64 * i;
-      v[i] = (e < E) ? row[e] : 0.0f;
-      if (e >= E) retired |= 1u << i;
+      key[i] = (e < E) ? route_key(row[e], e) : 0;     // 0 is below every real key
+      const uint32_t hv = (uint32_t)(key[i] >> 32);
+      lmax = hv > lmax ? hv : lmax;
     }
-    float my_v = 0.0f;
-    int my_i = 0;
-    for (int j = 0; j < k; ++j) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
+    // largest thr with at least k lane maxima >= thr
+    uint32_t thr = 0;
 #pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        // ascending e within the lane, so a strict '>' keeps the lower index on ties
-        if (!((retired >> i) & 1u) && (bi == 0x7fffffff || v[i] > bv)) {
-          bv = v[i];
-          bi = lane + 64 * i;
-        }
-      }
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = thr | (1u << bit);
+      if (__builtin_popcountll(__ballot(lmax >= c)) >= k) thr = c;
+    }
+    const uint64_t thr_key = (uint64_t)thr << 32;
+    int c = 0;
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, 64);
-        const int oi = __shfl_xor(bi, off, 64);
-        if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if ((bi & 63) == lane) retired |= 1u << (bi >> 6);
-      if (lane == j) {
-        my_v = bv;
-        my_i = bi;
+    for (int i = 0; i < NV; ++i) c += (key[i] >= thr_key) ? 1 : 0;
+    int incl = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    const int total = __builtin_amdgcn_readlane(incl, 63);
+    uint64_t mine = 0;
+    if (total <= 64) {
+      int pos = incl - c;
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        if (key[i] >= thr_key) cand[wv][pos++] = key[i];
+      __builtin_amdgcn_wave_barrier();
+      const uint64_t my = (lane < total) ? cand[wv][lane] : 0;
+      int rank = 0;
+      for (int j = 0; j < total; ++j) rank += (cand[wv][j] > my) ? 1 : 0;   // broadcast reads
+      if (lane < total && rank < k) sel[wv][rank] = my;
+      __builtin_amdgcn_wave_barrier();
+      if (lane < k) mine = sel[wv][lane];
+      __builtin_amdgcn_wave_barrier();
+    } else {
+      for (int j = 0; j < k; ++j) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) best = key[i] > best ? key[i] : best;
+        best = wave_max64(best);
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+          if (key[i] == best) key[i] = 0;              // keys are unique: only the winner
+        if (lane == j) mine = best;
       }
     }
-    const float m = __shfl(my_v, 0, 64);        // first pick is the maximum
-    float ex = (lane < k) ? expf(my_v - m) : 0.0f;
+    const float v = key_value(mine);
+    const float m = __shfl(v, 0, 64);                 // slot 0 holds the maximum
+    const float ex = (lane < k) ? expf(v - m) : 0.0f;
     float sum = ex;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
     if (lane < k) {
-      idx_out[t * k + lane] = my_i;
+      idx_out[t * k + lane] = key_index(mine);
       gates_out[t * k + lane] = ex / sum;
     }
   }
@@ -86,6 +147,8 @@ hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int32
   else if (nv <= 2) hipLaunchKernelGGL(route_topk_kernel<2>, grid, block, 0, s, logits, T, E, k, idx, gates);
   else if (nv <= 4) hipLaunchKernelGGL(route_topk_kernel<4>, grid, block, 0, s, logits, T, E, k, idx, gates);
   else if (nv <= 8) hipLaunchKernelGGL(route_topk_kernel<8>, grid, block, 0, s, logits, T, E, k, idx, gates);
+  else if (nv <= 12) hipLaunchKernelGGL(route_topk_kernel<12>, grid, block, 0, s, logits, T, E, k, idx, gates);
+  else if (nv <= 14) hipLaunchKernelGGL(route_topk_kernel<14>, grid, block, 0, s, logits, T, E, k, idx, gates);
   else hipLaunchKernelGGL(route_topk_kernel<16>, grid, block, 0, s, logits, T, E, k, idx, gates);
   return hipGetLastError();
 }
