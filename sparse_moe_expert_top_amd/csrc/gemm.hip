@@ -387,7 +387,10 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
 
   const int nblk = gridDim.x;
   const int b = blockIdx.x;
-  const int first = ((nblk & 7) == 0) ? ((b & 7) * (nblk >> 3) + (b >> 3)) : b;
+#ifndef MOE_XCD_MAP
+#define MOE_XCD_MAP 1
+#endif
+  const int first = (MOE_XCD_MAP && (nblk & 7) == 0) ? ((b & 7) * (nblk >> 3) + (b >> 3)) : b;
 
   for (int tile = first; tile < total; tile += nblk) {
     int g, mt, nt;

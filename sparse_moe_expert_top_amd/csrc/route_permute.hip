@@ -14,7 +14,7 @@ namespace moe {
 // ------------------------------------------------------------------------------ routing
 // One wavefront per token; lane l holds the logits of experts l, l+64, ... . Every logit
 // becomes a 64-bit key whose order is the routing order: the high word is the fp32 value
-// mapped to an unsigned order (after -0 -> +0, so the two zeros tie), the low word is the
+// bits mapped to an unsigned order (-0 -> +0 first, so the two zeros tie), the low word is the
 // complement of the expert index (equal values: lower index first). Keys are unique, so
 // "the k largest keys in descending order" is exactly the slot order.
 //
@@ -26,7 +26,8 @@ namespace moe {
 // Otherwise (many ties) k rounds of a wave arg-max pick them one by one. The softmax runs
 // in fp32 over the k picked values.
 __device__ __forceinline__ uint64_t route_key(float v, int e) {
-  const uint32_t b = __float_as_uint(v + 0.0f);
+  uint32_t b = __float_as_uint(v);
+  if (b == 0x80000000u) b = 0u;                     // -0 -> +0 on the bits (no float op)
   const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
   return ((uint64_t)o << 32) | (uint32_t)(~e);
 }

@@ -174,6 +174,28 @@ def test_route_ties(moe):
         assert rel_err(g_gates.cpu().numpy(), gates) <= FP32_TOL
 
 
+@pytest.mark.parametrize("T,E,k", [(1000, 1024, 32), (777, 1000, 16), (300, 65, 1), (300, 64, 32),
+                                   (500, 100, 32), (257, 896, 16), (129, 33, 33 - 1)])
+def test_route_shapes(moe, T, E, k):
+    """Envelope edges of the router: E not a multiple of 64, E = 1024, k = 1 and k = 32, and
+    rows that force the many-ties path (all equal; few distinct levels), next to rows with
+    extreme but finite values, signed zeros and subnormals."""
+    say(f"route T={T} E={E} k={k}")
+    rng = np.random.default_rng(T * 7 + E)
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    L[0] = 1.5                                                  # every logit equal
+    L[1] = rng.integers(0, 3, size=E).astype(np.float32)        # three levels: >64 ties at the cut
+    L[2, ::3] = -0.0
+    L[2, 1::3] = 0.0
+    L[3] = rng.choice(np.array([-3e38, 3e38, 1e-40, -1e-40, 0.0], np.float32), size=E)
+    L[4] = np.arange(E, dtype=np.float32)[::-1] * 1e-3          # strictly decreasing by index
+    idx, gates = oracle.route_topk(L, k)
+    g_idx, g_gates = moe.moe_route_topk(dev(L), k)
+    assert np.array_equal(g_idx.cpu().numpy(), idx)
+    assert rel_err(g_gates.cpu().numpy(), gates) <= FP32_TOL
+    assert float((g_gates.sum(1) - 1).abs().max()) <= 1e-5
+
+
 def test_permute_capacity_overflow(moe):
     """R_cap below the routed rows: flag raised, offsets clamped, dropped routes get -1."""
     cfg = LAYER_CONFIGS["tiny"]
