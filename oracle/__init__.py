@@ -16,6 +16,10 @@ What it computes, and where the pages define it:
   * expert layer forward/backward (`layer`) - "Kimi K3 ... Memory", "MoE 反向": the expert
     forward equations (a_e, o_e, y) and the router-probability gradient rewritten as
     <W_down^T dL/dy, a_e> so o_e is never needed.
+  * MXFP8 storage of the saved pre-activation (`mxfp8`) - "Kimi K3 ... Memory" (unified
+    activation manager; ledger summary): saved activations kept block-wise in FP8. Format
+    read as OCP MX v1.0 MXFP8 (E4M3 elements, 32-element blocks, E8M0 scales); the layer
+    backward takes h_store="mxfp8" to recompute from the stored value.
 
 Two numeric modes:
   * "X" (exact): no intermediate rounding; used for the mathematical invariants.

@@ -19,6 +19,7 @@ local experts, zero for non-local routes; an expert with no rows gets a zero gra
 """
 import numpy as np
 
+from . import mxfp8
 from .bf16 import bf16_round, bf16_widen
 from .situ import situ_glu_fwd, situ_glu_bwd
 
@@ -63,10 +64,17 @@ def expert_layer_fwd(x, w_gu, w_down, perm, H, beta=4.0, linear_beta=25.0, mode=
     return dict(y=_maybe_round(y, mode), h=h_all, a=a_all)
 
 
+def _stored_h(h, h_store):
+    """The pre-activation the backward reads: as saved in bf16, or after MXFP8 storage."""
+    return mxfp8.roundtrip(h) if h_store == "mxfp8" else h
+
+
 def expert_layer_bwd(x, dy, w_gu, w_down, perm, H, beta=4.0, linear_beta=25.0, mode="S",
-                     keep=False):
+                     keep=False, h_store="bf16"):
     """Grouped backward with dL/dy = dy; recomputes h from x (the re-dispatch).
 
+    h_store="mxfp8": the saved h went through MXFP8 storage (oracle.mxfp8), so the
+    activation and its gradient are recomputed from the stored value.
     Returns dict(dx [T,d], dw_gu [E_loc,2H,d], dw_down [E_loc,d,H], dp [T,k], dp_rows [R])
     and dh [R,2H] when keep=True.
     """
@@ -90,7 +98,7 @@ def expert_layer_bwd(x, dy, w_gu, w_down, perm, H, beta=4.0, linear_beta=25.0, m
         p = row_gate[r0:r1, None]
         X, dY = xf[tok], dyf[tok]
         Wgu, Wd = _f64(w_gu[e]), _f64(w_down[e])
-        h = _maybe_round(X @ Wgu.T, mode)
+        h = _stored_h(_maybe_round(X @ Wgu.T, mode), h_store)
         a = _maybe_round(situ_glu_fwd(h, H, beta, linear_beta), mode)
         G = dY @ Wd                                   # W_down^T dy, per row [n, H]
         dp_rows[r0:r1] = np.sum(G * a, axis=1)        # <W_down^T dy, a>
@@ -149,14 +157,22 @@ def token_layer_bwd(x_t, dy_t, idx_t, gates_t, w_gu, w_down, e_lo, H, beta=4.0,
     return _maybe_round(dx, mode), dp
 
 
-def dw_columns(x, dy, w_gu, w_down, perm, e, cols, H, beta=4.0, linear_beta=25.0, mode="S"):
+def dw_columns(x, dy, w_gu, w_down, perm, e, cols, H, beta=4.0, linear_beta=25.0, mode="S",
+               h_store="bf16"):
     """Weight gradients of local expert e restricted to intermediate columns `cols`.
 
     Returns (dw_gu_rows [2*len(cols), d] = rows cols then H+cols of dW_gu[e],
              dw_down_cols [d, len(cols)] = columns cols of dW_down[e]).
     SiTU-GLU is elementwise, so column j of h, a, dh depends only on columns j and j+H.
+    With h_store="mxfp8" the columns must cover whole 32-column blocks (a block shares one
+    scale), in ascending order.
     """
     cols = np.asarray(cols, dtype=np.int64)
+    if h_store == "mxfp8":
+        assert len(cols) % mxfp8.BLOCK == 0 and np.all(cols.reshape(-1, mxfp8.BLOCK) ==
+                                                      cols.reshape(-1, mxfp8.BLOCK)[:, :1] +
+                                                      np.arange(mxfp8.BLOCK))
+        assert np.all(cols.reshape(-1, mxfp8.BLOCK)[:, 0] % mxfp8.BLOCK == 0)
     off, row_token, row_gate = perm["offsets"], perm["row_token"], perm["row_gate"]
     r0, r1 = int(off[e]), int(off[e + 1])
     d = w_gu.shape[2]
@@ -169,7 +185,7 @@ def dw_columns(x, dy, w_gu, w_down, perm, e, cols, H, beta=4.0, linear_beta=25.0
     Wsel = _f64(np.concatenate([w_gu[e][cols], w_gu[e][H + cols]], axis=0))   # [2c, d]
     Wd = _f64(w_down[e][:, cols])                                              # [d, c]
     c = len(cols)
-    h = _maybe_round(X @ Wsel.T, mode)                                         # [n, 2c]
+    h = _stored_h(_maybe_round(X @ Wsel.T, mode), h_store)                     # [n, 2c]
     a = _maybe_round(situ_glu_fwd(h, c, beta, linear_beta), mode)
     G = dY @ Wd
     dh = _maybe_round(situ_glu_bwd(h, p * G, c, beta, linear_beta), mode)

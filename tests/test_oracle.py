@@ -450,3 +450,96 @@ def test_page_numbers_fix_the_shapes():
         g["routing"]["topk"], ep["local_experts"])
     sd = g["situ_defaults"]
     assert (shard.beta, shard.linear_beta) == (sd["beta"], sd["linear_beta"])
+
+
+# ------------------------------------------------------------------ MXFP8 storage of h
+def test_mx_e4m3_decode_matches_torch():
+    """All 256 E4M3 codes decode as torch's float8_e4m3fn (OCP E4M3) does."""
+    from oracle import mxfp8
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    got = mxfp8.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF]) and got[0x7E] == 448.0 and got[1] == 2.0 ** -9
+
+
+def test_mx_e4m3_encode_matches_torch():
+    """Round to nearest, ties to even, on fp32 inputs inside +-448: torch's cast is the
+    independent reference (every representable value, every midpoint, random values)."""
+    from oracle import mxfp8
+    pos = mxfp8.e4m3_decode(np.arange(127, dtype=np.uint8))
+    mids = (pos[1:] + pos[:-1]) / 2
+    rng = np.random.default_rng(0)
+    x = np.concatenate([pos, -pos, mids, -mids, rng.uniform(-448, 448, 50000),
+                        rng.standard_normal(50000) * 1e-2]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(mxfp8.e4m3_encode(x.astype(np.float64)), ref)
+
+
+def test_mx_e4m3_saturation_and_zero_sign():
+    from oracle import mxfp8
+    got = mxfp8.e4m3_encode(np.array([448.0, 449.0, 464.0, 1e6, -500.0, 0.0, -0.0, -1e-5]))
+    assert list(got) == [0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0x00, 0x80, 0x80]
+
+
+def test_mx_scale_exponent_rule():
+    """X = floor(log2 amax) - 8, clamped to [-127, 127]; zero blocks take -127."""
+    from oracle import mxfp8
+    amax = np.array([1.0, 0.75, 448.0, 511.0, 512.0, 0.0, 2.0 ** -130, 3e38, 2.0 ** -119])
+    assert list(mxfp8.block_scale_exp(amax)) == [-8, -9, 0, 0, 1, -127, -127, 119, -127]
+
+
+def test_mx_roundtrip_bounds():
+    """Per block: the largest magnitude lands in [256, 512) times 2^X; elements at or below
+    448 * 2^X are within half a quantum (2^-4 relative for normals, 2^(X-10) absolute for
+    subnormals); elements above saturate to 448 * 2^X; representable values are exact."""
+    from oracle import mxfp8
+    rng = np.random.default_rng(1)
+    v = rng.standard_normal((64, 256)) * np.exp(rng.uniform(-20, 20, size=(64, 1)))
+    c, s = mxfp8.quantize(v)
+    d = mxfp8.dequantize(c, s)
+    X = (s.astype(np.int64) - 127).repeat(32, axis=1)
+    sc = np.ldexp(1.0, X)
+    amax = np.abs(v).reshape(64, 8, 32).max(-1).repeat(32, axis=1)
+    assert np.all((amax / sc >= 256) & (amax / sc < 512))
+    sat = np.abs(v) > 448 * sc
+    assert np.all(np.abs(d[sat]) == 448 * sc[sat])
+    ok = ~sat
+    err = np.abs(d - v)[ok]
+    assert np.all(err <= np.maximum(2.0 ** -4 * np.abs(v[ok]), 2.0 ** -10 * sc[ok]) * (1 + 1e-12))
+    exact = mxfp8.e4m3_decode(rng.integers(0, 127, size=(16, 64)).astype(np.uint8)) * 2.0 ** 5
+    exact[:, ::32] = 448.0 * 2.0 ** 5                    # fixes each block's scale at X = 5
+    assert np.array_equal(mxfp8.roundtrip(exact), exact)
+
+
+def test_mx_layer_bwd_reduces_to_bf16_store_on_representable_h():
+    """With weights that make every h exactly representable in MXFP8, the MXFP8 store
+    changes nothing; with general weights the gradients move by at most a few percent."""
+    from oracle import layer, mxfp8
+    rng = np.random.default_rng(2)
+    T, d, H, E, k = 48, 32, 64, 4, 2
+    x = np.zeros((T, d)); x[np.arange(T), np.arange(T) % d] = 1.0          # one-hot rows
+    w_gu = mxfp8.e4m3_decode(rng.integers(0, 127, size=(E, 2 * H, d)).astype(np.uint8))
+    w_gu *= np.where(rng.random(w_gu.shape) < 0.5, -1.0, 1.0) * 2.0 ** -4
+    w_gu[:, ::32, :] = 448 * 2.0 ** -4      # every 32-row block holds its amax: X = -4, exact
+    w_down = rng.standard_normal((E, d, H)) * 0.1
+    dy = rng.standard_normal((T, d))
+    idx = np.stack([np.arange(T) % E, (np.arange(T) + 1) % E], 1).astype(np.int32)
+    gates = np.full((T, k), 0.5)
+    perm = oracle.permute(idx, gates, 0, E)
+    # one-hot rows: h[r] is a column of w_gu[e], so each 32-column block of h is representable
+    ref = layer.expert_layer_bwd(x, dy, w_gu, w_down, perm, H, mode="X")
+    got = layer.expert_layer_bwd(x, dy, w_gu, w_down, perm, H, mode="X", h_store="mxfp8")
+    h = np.concatenate([x[perm["row_token"][perm["offsets"][e]:perm["offsets"][e + 1]]] @ w_gu[e].T
+                        for e in range(E)])
+    assert np.array_equal(mxfp8.roundtrip(h), h)
+    for key in ("dx", "dw_gu", "dw_down", "dp"):
+        assert np.array_equal(got[key], ref[key]), key
+    w2 = rng.standard_normal((E, 2 * H, d)) * 0.3
+    x2 = rng.standard_normal((T, d))
+    r2 = layer.expert_layer_bwd(x2, dy, w2, w_down, perm, H, mode="X")
+    g2 = layer.expert_layer_bwd(x2, dy, w2, w_down, perm, H, mode="X", h_store="mxfp8")
+    for key in ("dx", "dw_gu", "dw_down", "dp"):
+        e = np.max(np.abs(g2[key] - r2[key])) / np.max(np.abs(r2[key]))
+        assert 0 < e < 0.1, (key, e)
