@@ -189,6 +189,56 @@ moe_status moe_expert_bwd(const void* dy, const void* x, const void* h,
                           void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * MXFP8 storage of the saved pre-activation ("Kimi K3 ... Memory", unified activation
+ * manager and ledger summary: most saved activations are kept block-wise in FP8, which
+ * halves them again). Format (the pages do not fix one; read as OCP Microscaling v1.0
+ * MXFP8): rows are cut into blocks of 32 consecutive elements; each block stores a scale
+ * byte s = X + 127 with X = floor(log2(max |v|)) - 8 clamped to [-127, 127] (-127 for an
+ * all-zero block), and each element the E4M3 code of v / 2^X (1 sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits; round to nearest, ties to even; saturate to +-448; the sign is
+ * kept when the magnitude rounds to zero). The value read back is E4M3(code) * 2^X.
+ * A row of n elements takes n code bytes plus n/32 scale bytes.
+ */
+
+/*
+ * moe_grouped_gemm_gate_up_mx - moe_grouped_gemm_gate_up with the saved h stored as MXFP8:
+ *   h_codes [R_cap, 2H] uint8 out, h_scales [R_cap, 2H/32] uint8 out hold the MXFP8 form of
+ *   the bf16 h that `a` is computed from; a [R_cap, H] bf16 out as in the bf16 call.
+ * Same arguments, limits and errors otherwise; h_codes must be 16-byte aligned.
+ */
+moe_status moe_grouped_gemm_gate_up_mx(const void* x, const int32_t* row_token,
+                                       const int32_t* expert_offsets, int E_loc, int64_t R_cap,
+                                       int d, int H, const void* w_gu, float beta,
+                                       float linear_beta, void* h_codes, void* h_scales,
+                                       void* a, hipStream_t stream);
+
+/*
+ * moe_expert_bwd_mx - moe_expert_bwd reading the saved h from MXFP8 (h_codes [R_cap, 2H],
+ * h_scales [R_cap, 2H/32], as written by moe_grouped_gemm_gate_up_mx): a, dp and dh are
+ * recomputed from the stored value. Same workspace, outputs and errors as moe_expert_bwd.
+ */
+moe_status moe_expert_bwd_mx(const void* dy, const void* x, const void* h_codes,
+                             const void* h_scales, const int32_t* row_token,
+                             const float* row_gate, const int32_t* slot_row,
+                             const int32_t* expert_offsets, int64_t T, int k, int E_loc,
+                             int64_t R_cap, int d, int H, const void* w_gu, const void* w_down,
+                             float beta, float linear_beta, void* dx, float* dw_gu,
+                             float* dw_down, float* dp, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+/*
+ * moe_mxfp8_quantize - v [rows, n] bf16 -> codes [rows, n] uint8, scales [rows, n/32] uint8
+ * in the format above. moe_mxfp8_dequantize - the inverse, out [rows, n] bf16 (exact for
+ * values of magnitude >= 2^-126; E4M3 values carry 4 significant bits).
+ * n must be a multiple of 32 (MOE_ERR_UNSUPPORTED otherwise); v, codes and out 16-byte
+ * aligned; scales has no alignment requirement.
+ */
+moe_status moe_mxfp8_quantize(const void* v, int64_t rows, int n, void* codes, void* scales,
+                              hipStream_t stream);
+moe_status moe_mxfp8_dequantize(const void* codes, const void* scales, int64_t rows, int n,
+                                void* out, hipStream_t stream);
+
+/*
  * moe_router_bwd - gradient through the softmax over the kept logits: with p the gates and
  * g = dL/dp, dlogit_kept[t, j] = p_j (g_j - sum_i p_i g_i) (fp32). Logits that were not kept
  * do not reach the output. Only meaningful when all k routes of a token are local (or dp

@@ -141,6 +141,24 @@ def layer_inputs(cfg: LayerConfig | str, seed: int = 0, T: int | None = None) ->
     return dict(logits=logits, x=x, w_gu=w_gu, w_down=w_down, dy=dy)
 
 
+def dyadic_layer_inputs(cfg: LayerConfig | str, seed: int = 0) -> dict:
+    """layer_inputs with x and w_gu on coarse dyadic grids, so every partial sum of
+    h = x . w_gu^T is exact in fp32 (x in {0, +-1, +-2} 2^-3, w_gu in {-7..7} 2^-7; the sum
+    over d <= 4096 terms needs at most 17 significant bits). Any correct GEMM then produces
+    the same h, and so the same bf16 h, as the fp64 oracle: used where the stored form of h
+    is compared bit for bit. logits, w_down and dy are drawn as in layer_inputs."""
+    if isinstance(cfg, str):
+        cfg = LAYER_CONFIGS[cfg]
+    assert cfg.d <= 4096
+    out = layer_inputs(cfg, seed)
+    rng = np.random.default_rng(seed + 1000)
+    x = rng.integers(-2, 3, size=(cfg.T, cfg.d)).astype(np.float32) * 0.125
+    w_gu = rng.integers(-7, 8, size=(cfg.E_loc, 2 * cfg.H, cfg.d)).astype(np.float32) / 128.0
+    out["x"] = f32_to_bf16_bits(x)
+    out["w_gu"] = f32_to_bf16_bits(w_gu)
+    return out
+
+
 def situ_inputs(R: int, H: int, seed: int = 0, h_std: float = 3.0) -> dict:
     """Draw h bf16 [R, 2H] ~ N(0, h_std^2) and da bf16 [R, H] ~ N(0, 1), in that order."""
     rng = np.random.default_rng(seed)

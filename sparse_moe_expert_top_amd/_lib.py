@@ -54,6 +54,12 @@ _SIGS = {
     "moe_expert_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I64, _I, _I, _I64, _I, _I, _P, _P, _F,
                             _F, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_router_bwd": (_I, [_P, _P, _I64, _I, _P, _P]),
+    "moe_grouped_gemm_gate_up_mx": (_I, [_P, _P, _P, _I, _I64, _I, _I, _P, _F, _F, _P, _P, _P,
+                                         _P]),
+    "moe_expert_bwd_mx": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I, _I, _I64, _I, _I, _P,
+                               _P, _F, _F, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_mxfp8_quantize": (_I, [_P, _I64, _I, _P, _P, _P]),
+    "moe_mxfp8_dequantize": (_I, [_P, _P, _I64, _I, _P, _P]),
     "moe_workspace_size": (_I, [_I, _I64, _I, _I, _I, _I, _I64, ctypes.POINTER(_SZ)]),
 }
 
@@ -263,6 +269,88 @@ def moe_expert_bwd(dy, x, h, perm, w_gu, w_down, R_cap, beta=4.0, linear_beta=25
         _ptr(w_down), beta, linear_beta, _ptr(dx), _ptr(dw_gu), _ptr(dw_down), _ptr(dp),
         _ptr(ws), ws.numel(), _stream(stream)))
     return dx, dw_gu, dw_down, dp
+
+
+def moe_grouped_gemm_gate_up_mx(x, row_token, offsets, w_gu, R_cap, beta=4.0,
+                                linear_beta=25.0, h_codes=None, h_scales=None, a=None,
+                                stream=None):
+    """moe_grouped_gemm_gate_up storing the saved h as MXFP8 (codes, scale bytes)."""
+    E_loc, H2, d = w_gu.shape
+    H = H2 // 2
+    _need(x, "x", torch.bfloat16)
+    _need(w_gu, "w_gu", torch.bfloat16)
+    _need(row_token, "row_token", torch.int32)
+    _need(offsets, "offsets", torch.int32, (E_loc + 1,))
+    dev = x.device
+    h_codes = torch.empty((R_cap, 2 * H), dtype=torch.uint8, device=dev) if h_codes is None else h_codes
+    h_scales = (torch.empty((R_cap, 2 * H // 32), dtype=torch.uint8, device=dev)
+                if h_scales is None else h_scales)
+    a = torch.empty((R_cap, H), dtype=torch.bfloat16, device=dev) if a is None else a
+    _need(h_codes, "h_codes", torch.uint8, (R_cap, 2 * H))
+    _need(h_scales, "h_scales", torch.uint8, (R_cap, 2 * H // 32))
+    _need(a, "a", torch.bfloat16)
+    _check("moe_grouped_gemm_gate_up_mx", load().moe_grouped_gemm_gate_up_mx(
+        _ptr(x), _ptr(row_token), _ptr(offsets), E_loc, R_cap, d, H, _ptr(w_gu), beta,
+        linear_beta, _ptr(h_codes), _ptr(h_scales), _ptr(a), _stream(stream)))
+    return h_codes, h_scales, a
+
+
+def moe_expert_bwd_mx(dy, x, h_codes, h_scales, perm, w_gu, w_down, R_cap, beta=4.0,
+                      linear_beta=25.0, dx=None, dw_gu=None, dw_down=None, dp=None, ws=None,
+                      stream=None):
+    """moe_expert_bwd reading the saved h from MXFP8 codes and scale bytes."""
+    E_loc, H2, d = w_gu.shape
+    H = H2 // 2
+    T, k = perm["slot_row"].shape
+    _need(dy, "dy", torch.bfloat16, (T, d))
+    _need(x, "x", torch.bfloat16, (T, d))
+    _need(h_codes, "h_codes", torch.uint8)
+    _need(h_scales, "h_scales", torch.uint8)
+    _need(w_gu, "w_gu", torch.bfloat16)
+    _need(w_down, "w_down", torch.bfloat16, (E_loc, d, H))
+    dev = dy.device
+    dx = torch.empty((T, d), dtype=torch.bfloat16, device=dev) if dx is None else dx
+    dw_gu = torch.empty((E_loc, 2 * H, d), dtype=torch.float32, device=dev) if dw_gu is None else dw_gu
+    dw_down = torch.empty((E_loc, d, H), dtype=torch.float32, device=dev) if dw_down is None else dw_down
+    dp = torch.empty((T, k), dtype=torch.float32, device=dev) if dp is None else dp
+    _need(dx, "dx", torch.bfloat16, (T, d))
+    _need(dw_gu, "dw_gu", torch.float32, (E_loc, 2 * H, d))
+    _need(dw_down, "dw_down", torch.float32, (E_loc, d, H))
+    _need(dp, "dp", torch.float32, (T, k))
+    need = workspace_size(MOE_WS_EXPERT_BWD, T=T, E_loc=E_loc, k=k, d=d, H=H, R_cap=R_cap)
+    ws = _ws(need, dev) if ws is None else ws
+    _check("moe_expert_bwd_mx", load().moe_expert_bwd_mx(
+        _ptr(dy), _ptr(x), _ptr(h_codes), _ptr(h_scales), _ptr(perm["row_token"]),
+        _ptr(perm["row_gate"]), _ptr(perm["slot_row"]), _ptr(perm["offsets"]), T, k, E_loc,
+        R_cap, d, H, _ptr(w_gu), _ptr(w_down), beta, linear_beta, _ptr(dx), _ptr(dw_gu),
+        _ptr(dw_down), _ptr(dp), _ptr(ws), ws.numel(), _stream(stream)))
+    return dx, dw_gu, dw_down, dp
+
+
+def moe_mxfp8_quantize(v, codes=None, scales=None, stream=None):
+    """bf16 [rows, n] -> (codes uint8 [rows, n], scale bytes uint8 [rows, n/32])."""
+    rows, n = v.shape
+    _need(v, "v", torch.bfloat16)
+    codes = torch.empty((rows, n), dtype=torch.uint8, device=v.device) if codes is None else codes
+    scales = (torch.empty((rows, n // 32), dtype=torch.uint8, device=v.device)
+              if scales is None else scales)
+    _need(codes, "codes", torch.uint8, (rows, n))
+    _need(scales, "scales", torch.uint8, (rows, n // 32))
+    _check("moe_mxfp8_quantize", load().moe_mxfp8_quantize(_ptr(v), rows, n, _ptr(codes),
+                                                           _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def moe_mxfp8_dequantize(codes, scales, out=None, stream=None):
+    """(codes, scale bytes) -> bf16 [rows, n]."""
+    rows, n = codes.shape
+    _need(codes, "codes", torch.uint8)
+    _need(scales, "scales", torch.uint8, (rows, n // 32))
+    out = torch.empty((rows, n), dtype=torch.bfloat16, device=codes.device) if out is None else out
+    _need(out, "out", torch.bfloat16, (rows, n))
+    _check("moe_mxfp8_dequantize", load().moe_mxfp8_dequantize(_ptr(codes), _ptr(scales), rows,
+                                                               n, _ptr(out), _stream(stream)))
+    return out
 
 
 def moe_router_bwd(gates, dp, out=None, stream=None):

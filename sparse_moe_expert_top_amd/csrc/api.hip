@@ -158,6 +158,25 @@ moe_status moe_grouped_gemm_gate_up(const void* x, const int32_t* row_token,
                                         (uint16_t*)a, stream));
 }
 
+moe_status moe_grouped_gemm_gate_up_mx(const void* x, const int32_t* row_token,
+                                       const int32_t* expert_offsets, int E_loc, int64_t R_cap,
+                                       int d, int H, const void* w_gu, float beta,
+                                       float linear_beta, void* h_codes, void* h_scales,
+                                       void* a, hipStream_t stream) {
+  if (E_loc < 1 || R_cap < 0) return MOE_ERR_SHAPE;
+  if (E_loc > 1024 || !layer_dims_ok(d, H) || R_cap >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  if (!(beta > 0.0f) || !(linear_beta > 0.0f)) return MOE_ERR_SHAPE;
+  if (!expert_offsets || !w_gu) return MOE_ERR_NULL;
+  if (R_cap == 0) return MOE_OK;
+  if (!x || !row_token || !h_codes || !h_scales || !a) return MOE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_gu) || !aligned16(h_codes) || !aligned16(a))
+    return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_gemm_gate_up_mx((const uint16_t*)x, row_token, expert_offsets, E_loc,
+                                           R_cap, d, H, (const uint16_t*)w_gu,
+                                           make_situ_coef(beta, linear_beta), (uint8_t*)h_codes,
+                                           (uint8_t*)h_scales, (uint16_t*)a, stream));
+}
+
 moe_status situ_glu_fwd(const void* h, int64_t R, int H, float beta, float linear_beta,
                         void* a, void* ws, size_t ws_bytes, hipStream_t stream) {
   (void)ws;
@@ -214,13 +233,14 @@ moe_status moe_grouped_gemm_down_combine(const void* a, const int32_t* expert_of
   return hip_status(launch_unpermute(rows, slot_row, nullptr, T, k, d, (uint16_t*)y, stream));
 }
 
-moe_status moe_expert_bwd(const void* dy, const void* x, const void* h,
-                          const int32_t* row_token, const float* row_gate,
-                          const int32_t* slot_row, const int32_t* expert_offsets, int64_t T,
-                          int k, int E_loc, int64_t R_cap, int d, int H, const void* w_gu,
-                          const void* w_down, float beta, float linear_beta, void* dx,
-                          float* dw_gu, float* dw_down, float* dp, void* ws, size_t ws_bytes,
-                          hipStream_t stream) {
+static moe_status expert_bwd_impl(const void* dy, const void* x, const void* h,
+                                  const void* h_codes, const void* h_scales,
+                                  const int32_t* row_token, const float* row_gate,
+                                  const int32_t* slot_row, const int32_t* expert_offsets,
+                                  int64_t T, int k, int E_loc, int64_t R_cap, int d, int H,
+                                  const void* w_gu, const void* w_down, float beta,
+                                  float linear_beta, void* dx, float* dw_gu, float* dw_down,
+                                  float* dp, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (T < 0 || k < 1 || E_loc < 1 || R_cap < 0) return MOE_ERR_SHAPE;
   if (k > 32 || E_loc > 1024 || !layer_dims_ok(d, H) || R_cap >= (int64_t)1 << 31)
     return MOE_ERR_UNSUPPORTED;
@@ -228,10 +248,11 @@ moe_status moe_expert_bwd(const void* dy, const void* x, const void* h,
   if (!(beta > 0.0f) || !(linear_beta > 0.0f)) return MOE_ERR_SHAPE;
   if (!expert_offsets || !w_gu || !w_down || !dw_gu || !dw_down) return MOE_ERR_NULL;
   if (T > 0 && (!dy || !x || !slot_row || !dx || !dp)) return MOE_ERR_NULL;
-  if (R_cap > 0 && (!h || !row_token || !row_gate || !ws)) return MOE_ERR_NULL;
+  if (R_cap > 0 && ((!h && !(h_codes && h_scales)) || !row_token || !row_gate || !ws))
+    return MOE_ERR_NULL;
   const size_t need = bwd_dh_bytes(R_cap, H) + bwd_ov_bytes(R_cap, d, H) + bwd_dp_bytes(R_cap, H);
   if (ws_bytes < need) return MOE_ERR_WORKSPACE;
-  const void* ptrs[] = {dy, x, h, w_gu, w_down, dx, dw_gu, dw_down, ws};
+  const void* ptrs[] = {dy, x, h, h_codes, w_gu, w_down, dx, dw_gu, dw_down, ws};
   for (const void* q : ptrs)
     if (q && !aligned16(q)) return MOE_ERR_UNSUPPORTED;
   const SituCoef c = make_situ_coef(beta, linear_beta);
@@ -242,8 +263,8 @@ moe_status moe_expert_bwd(const void* dy, const void* x, const void* h,
   hipError_t e = hipSuccess;
   if (R_cap > 0) {
     e = launch_gemm_da((const uint16_t*)dy, row_token, expert_offsets, E_loc, R_cap, d, H,
-                       (const uint16_t*)w_down, (const uint16_t*)h, row_gate, c, dh, ov, dpp,
-                       stream);
+                       (const uint16_t*)w_down, (const uint16_t*)h, (const uint8_t*)h_codes,
+                       (const uint8_t*)h_scales, row_gate, c, dh, ov, dpp, stream);
     if (e != hipSuccess) return hip_status(e);
   }
   // weight gradients: every expert's slice is written (zeros when it has no rows)
@@ -263,6 +284,55 @@ moe_status moe_expert_bwd(const void* dy, const void* x, const void* h,
   if (e != hipSuccess) return hip_status(e);
   return hip_status(launch_dp_reduce_scatter(dpp, gemm_da_slots(H), R_cap, expert_offsets,
                                              E_loc, slot_row, T, k, dp, stream));
+}
+
+moe_status moe_expert_bwd(const void* dy, const void* x, const void* h,
+                          const int32_t* row_token, const float* row_gate,
+                          const int32_t* slot_row, const int32_t* expert_offsets, int64_t T,
+                          int k, int E_loc, int64_t R_cap, int d, int H, const void* w_gu,
+                          const void* w_down, float beta, float linear_beta, void* dx,
+                          float* dw_gu, float* dw_down, float* dp, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  if (R_cap > 0 && !h) return MOE_ERR_NULL;
+  return expert_bwd_impl(dy, x, h, nullptr, nullptr, row_token, row_gate, slot_row,
+                         expert_offsets, T, k, E_loc, R_cap, d, H, w_gu, w_down, beta,
+                         linear_beta, dx, dw_gu, dw_down, dp, ws, ws_bytes, stream);
+}
+
+moe_status moe_expert_bwd_mx(const void* dy, const void* x, const void* h_codes,
+                             const void* h_scales, const int32_t* row_token,
+                             const float* row_gate, const int32_t* slot_row,
+                             const int32_t* expert_offsets, int64_t T, int k, int E_loc,
+                             int64_t R_cap, int d, int H, const void* w_gu, const void* w_down,
+                             float beta, float linear_beta, void* dx, float* dw_gu,
+                             float* dw_down, float* dp, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  if (R_cap > 0 && (!h_codes || !h_scales)) return MOE_ERR_NULL;
+  return expert_bwd_impl(dy, x, nullptr, h_codes, h_scales, row_token, row_gate, slot_row,
+                         expert_offsets, T, k, E_loc, R_cap, d, H, w_gu, w_down, beta,
+                         linear_beta, dx, dw_gu, dw_down, dp, ws, ws_bytes, stream);
+}
+
+moe_status moe_mxfp8_quantize(const void* v, int64_t rows, int n, void* codes, void* scales,
+                              hipStream_t stream) {
+  if (rows < 0 || n < 1) return MOE_ERR_SHAPE;
+  if (n % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!v || !codes || !scales) return MOE_ERR_NULL;
+  if (!aligned16(v) || !aligned16(codes)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_mx_quantize((const uint16_t*)v, rows, n, (uint8_t*)codes,
+                                       (uint8_t*)scales, stream));
+}
+
+moe_status moe_mxfp8_dequantize(const void* codes, const void* scales, int64_t rows, int n,
+                                void* out, hipStream_t stream) {
+  if (rows < 0 || n < 1) return MOE_ERR_SHAPE;
+  if (n % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!codes || !scales || !out) return MOE_ERR_NULL;
+  if (!aligned16(codes) || !aligned16(out)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_mx_dequantize((const uint8_t*)codes, (const uint8_t*)scales, rows, n,
+                                         (uint16_t*)out, stream));
 }
 
 moe_status moe_router_bwd(const float* gates, const float* dp, int64_t T, int k,

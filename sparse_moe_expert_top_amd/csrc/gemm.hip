@@ -46,12 +46,17 @@
 
 #include "common.h"
 #include "launch.h"
+#include "mxfp8.h"
 #include "situ_math.h"
 
 namespace moe {
 
 enum BKind { B_ROWS = 0, B_KOUT = 1 };
-enum Epi { EPI_GATEUP = 0, EPI_ROWS_SCALED = 1, EPI_ROWS = 2, EPI_DA = 3, EPI_F32 = 4 };
+enum Epi {
+  EPI_GATEUP = 0, EPI_ROWS_SCALED = 1, EPI_ROWS = 2, EPI_DA = 3, EPI_F32 = 4,
+  EPI_GATEUP_MX = 5,   // gate_up storing h as MXFP8 codes + scales
+  EPI_DA_MX = 6        // dA reading h from MXFP8 codes + scales
+};
 
 struct GemmArgs {
   const uint16_t* A;
@@ -77,6 +82,10 @@ struct GemmArgs {
   int64_t f_gstride;
   const float* row_scale;
   const uint16_t* hsrc;
+  uint8_t* q0;         // MXFP8 h codes [R, 2H] and scale bytes [R, 2H/32] (gate_up, stored)
+  uint8_t* s0;
+  const uint8_t* qsrc; // MXFP8 h codes and scales (dA, read)
+  const uint8_t* ssrc;
   float* dp_part;
   int64_t dp_ld;
   SituCoef sc;
@@ -283,7 +292,10 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
   static_assert(LA * 1024 * NW == BM * BK * 2 && LB * 1024 * NW == BN * BK * 2, "loads");
   static_assert(LA >= 1 && LB >= 1 && (NS == 2 || NS == 4), "stage geometry");
   static_assert(!KRAG || BKIND == B_KOUT, "weight gradients read B k-outer");
-  static_assert(EPI != EPI_GATEUP || (FN % 2 == 0), "gate/linear pairs");
+  constexpr bool IS_GU = (EPI == EPI_GATEUP || EPI == EPI_GATEUP_MX);
+  constexpr bool IS_DA = (EPI == EPI_DA || EPI == EPI_DA_MX);
+  constexpr bool HMX = (EPI == EPI_GATEUP_MX || EPI == EPI_DA_MX);
+  static_assert(!IS_GU || (FN % 2 == 0), "gate/linear pairs");
   static_assert(BK == 32 || BK == 64, "stage depth");
 
   // One LDS ring for both operands; after the k-loop it doubles as the epilogue's staging.
@@ -464,7 +476,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
         const int row = byte / (BK * 2);
         const int c = ((byte % (BK * 2)) >> 4) ^ rswz<BK>(row);
         int wrow;
-        if constexpr (EPI == EPI_GATEUP) {
+        if constexpr (IS_GU) {
           const int w = row / WN, qq = row % WN;
           const int jj = min(j0 + w * (WN / 2) + (qq % (WN / 2)), p.H - 1);
           wrow = (qq < WN / 2) ? jj : p.H + jj;
@@ -731,8 +743,10 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
         for (int v = 0; v < 16; ++v)
           st[((v >> 2) * 8 + (lane >> 5) * 4 + (v & 3)) * EPS + j * 32 + (lane & 31)] = acc[i][j][v];
       const int rblk = m0 + wm * WM + i * 32;            // tile-relative row of block row 0
-      if constexpr (EPI == EPI_GATEUP) {
-        // lane: 8 gate columns (cc) of row (ps*16 + lane/4) and the matching 8 linear columns
+      if constexpr (IS_GU) {
+        // lane: 8 gate columns (cc) of row (ps*16 + lane/4) and the matching 8 linear columns;
+        // the 4 lanes of a row hold 32 consecutive (32-aligned) gate and linear columns each:
+        // one MXFP8 block of each
         const int cc = lane & 3;
 #pragma unroll
         for (int ps = 0; ps < 2; ++ps) {
@@ -760,8 +774,31 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
                                     situ_fwd<B4>(bf16_hi(hg[q]), bf16_hi(hl[q]), p.sc));
             };
             if (p.sc.b4) act(std::true_type{}); else act(std::false_type{});
-            st_row16(&p.o0[r * p.ld0 + jj], hg);
-            st_row16(&p.o0[r * p.ld0 + p.H + jj], hl);
+            if constexpr (HMX) {
+              // the stored h is MXFP8 of the bf16 h that `a` was computed from
+              float gb[8], lb[8];
+              float mg = 0.0f, ml = 0.0f;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                gb[2 * q] = bf16_lo(hg[q]); gb[2 * q + 1] = bf16_hi(hg[q]);
+                lb[2 * q] = bf16_lo(hl[q]); lb[2 * q + 1] = bf16_hi(hl[q]);
+                mg = fmaxf(mg, fmaxf(fabsf(gb[2 * q]), fabsf(gb[2 * q + 1])));
+                ml = fmaxf(ml, fmaxf(fabsf(lb[2 * q]), fabsf(lb[2 * q + 1])));
+              }
+              const uint32_t sg = mx_scale_byte(mx_amax4(mg));
+              const uint32_t sl = mx_scale_byte(mx_amax4(ml));
+              uint8_t* qr = p.q0 + r * (2 * (int64_t)p.H);
+              *(u32x2*)&qr[jj] = mx_encode8(gb, sg);
+              *(u32x2*)&qr[p.H + jj] = mx_encode8(lb, sl);
+              if (cc == 0) {
+                uint8_t* sr = p.s0 + r * (2 * (int64_t)p.H / kMxBlock);
+                sr[jj / kMxBlock] = (uint8_t)sg;
+                sr[(p.H + jj) / kMxBlock] = (uint8_t)sl;
+              }
+            } else {
+              st_row16(&p.o0[r * p.ld0 + jj], hg);
+              st_row16(&p.o0[r * p.ld0 + p.H + jj], hl);
+            }
             st_row16(&p.o1[r * p.ld1 + jj], av);
           }
         }
@@ -786,13 +823,37 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
               for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(cv[2 * q] * sc, cv[2 * q + 1] * sc);
               st_row16(&p.o0[r * p.ld0 + col], o);
             }
-          } else if constexpr (EPI == EPI_DA) {
+          } else if constexpr (IS_DA) {
             if (rblk + row < Mg && col < p.N) {
               const int64_t r = r0 + rblk + row;
               const float pr = p.row_scale[r];
-              const uint16_t* hr = p.hsrc + r * (2 * (int64_t)p.H);
-              const u32x4 hg = *(const u32x4*)&hr[col];
-              const u32x4 hl = *(const u32x4*)&hr[p.H + col];
+              // the saved pre-activation of these 8 columns (gate half, linear half): bf16
+              // pairs, or MXFP8 decoded to fp32
+              u32x4 hg = {0u, 0u, 0u, 0u}, hl = {0u, 0u, 0u, 0u};
+              u32x2 qg = {0u, 0u}, ql = {0u, 0u};
+              int xg = 0, xl = 0;
+              if constexpr (HMX) {
+                const uint8_t* qr = p.qsrc + r * (2 * (int64_t)p.H);
+                const uint8_t* sr = p.ssrc + r * (2 * (int64_t)p.H / kMxBlock);
+                qg = *(const u32x2*)&qr[col];
+                ql = *(const u32x2*)&qr[p.H + col];
+                xg = (int)sr[col / kMxBlock] - 127;
+                xl = (int)sr[(p.H + col) / kMxBlock] - 127;
+              } else {
+                const uint16_t* hr = p.hsrc + r * (2 * (int64_t)p.H);
+                hg = *(const u32x4*)&hr[col];
+                hl = *(const u32x4*)&hr[p.H + col];
+              }
+              auto hgv = [&](int i) __attribute__((always_inline)) {
+                if constexpr (HMX)
+                  return __builtin_amdgcn_ldexpf(e4m3_decode((qg[i >> 2] >> (8 * (i & 3))) & 0xFFu), xg);
+                else return (i & 1) ? bf16_hi(hg[i >> 1]) : bf16_lo(hg[i >> 1]);
+              };
+              auto hlv = [&](int i) __attribute__((always_inline)) {
+                if constexpr (HMX)
+                  return __builtin_amdgcn_ldexpf(e4m3_decode((ql[i >> 2] >> (8 * (i & 3))) & 0xFFu), xl);
+                else return (i & 1) ? bf16_hi(hl[i >> 1]) : bf16_lo(hl[i >> 1]);
+              };
               u32x4 og, ol, oa;
               float acc_p = 0.0f;
               auto grad = [&](auto b4) {
@@ -800,8 +861,8 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                   float a0, dg0, dl0, a1, dg1, dl1;
-                  situ_bwd<B4>(bf16_lo(hg[q]), bf16_lo(hl[q]), pr * cv[2 * q], p.sc, a0, dg0, dl0);
-                  situ_bwd<B4>(bf16_hi(hg[q]), bf16_hi(hl[q]), pr * cv[2 * q + 1], p.sc, a1, dg1,
+                  situ_bwd<B4>(hgv(2 * q), hlv(2 * q), pr * cv[2 * q], p.sc, a0, dg0, dl0);
+                  situ_bwd<B4>(hgv(2 * q + 1), hlv(2 * q + 1), pr * cv[2 * q + 1], p.sc, a1, dg1,
                                dl1);
                   const float ab0 = round_bf16(a0), ab1 = round_bf16(a1);
                   acc_p += cv[2 * q] * ab0;
@@ -820,7 +881,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
             }
           }
         }
-        if constexpr (EPI == EPI_DA) {
+        if constexpr (IS_DA) {
           // <G, a> over this wavefront's 64 columns: sum the 8 lanes that share a row
           const int slot = nt * C::WGN + wn;
 #pragma unroll
@@ -916,6 +977,22 @@ hipError_t launch_gemm_gate_up(const uint16_t* x, const int32_t* row_token,
       p, mragged_tile_bound(R_cap, E_loc, CGU::BM, p.n_tiles), s);
 }
 
+hipError_t launch_gemm_gate_up_mx(const uint16_t* x, const int32_t* row_token,
+                                  const int32_t* offsets, int E_loc, int64_t R_cap, int d,
+                                  int H, const uint16_t* w_gu, SituCoef c, uint8_t* h_codes,
+                                  uint8_t* h_scales, uint16_t* a, hipStream_t s) {
+  GemmArgs p = blank_args();
+  p.A = x; p.lda = d; p.a_gather = row_token;
+  p.B = w_gu; p.ldb = d; p.b_gstride = (int64_t)2 * H * d;
+  p.offsets = offsets; p.G = E_loc;
+  p.N = 2 * H; p.K = d; p.H = H;
+  p.n_tiles = (H + CGU::BN / 2 - 1) / (CGU::BN / 2);
+  p.q0 = h_codes; p.s0 = h_scales; p.o1 = a; p.ld1 = H;
+  p.sc = c;
+  return run_gemm<CGU, false, B_ROWS, EPI_GATEUP_MX>(
+      p, mragged_tile_bound(R_cap, E_loc, CGU::BM, p.n_tiles), s);
+}
+
 hipError_t launch_gemm_down(const uint16_t* a, const int32_t* offsets, const float* row_gate,
                             int E_loc, int64_t R_cap, int H, int d, const uint16_t* w_down,
                             uint16_t* rows_out, hipStream_t s) {
@@ -934,8 +1011,9 @@ int gemm_da_slots(int H) { return ((H + CDA::BN - 1) / CDA::BN) * CDA::WGN; }
 
 hipError_t launch_gemm_da(const uint16_t* dy, const int32_t* row_token, const int32_t* offsets,
                           int E_loc, int64_t R_cap, int d, int H, const uint16_t* w_down,
-                          const uint16_t* h, const float* row_gate, SituCoef c, uint16_t* dh,
-                          uint16_t* pa, float* dp_part, hipStream_t s) {
+                          const uint16_t* h, const uint8_t* h_codes, const uint8_t* h_scales,
+                          const float* row_gate, SituCoef c, uint16_t* dh, uint16_t* pa,
+                          float* dp_part, hipStream_t s) {
   GemmArgs p = blank_args();
   p.A = dy; p.lda = d; p.a_gather = row_token;
   p.B = w_down; p.ldb = H; p.b_gstride = (int64_t)d * H;      // B(n=j, k) = w_down[e][k][j]
@@ -944,7 +1022,11 @@ hipError_t launch_gemm_da(const uint16_t* dy, const int32_t* row_token, const in
   p.n_tiles = (H + CDA::BN - 1) / CDA::BN;
   p.o0 = dh; p.ld0 = 2 * H; p.o1 = pa; p.ld1 = H;
   p.row_scale = row_gate; p.hsrc = h; p.dp_part = dp_part; p.dp_ld = R_cap;
+  p.qsrc = h_codes; p.ssrc = h_scales;
   p.sc = c;
+  if (h_codes)
+    return run_gemm<CDA, false, B_KOUT, EPI_DA_MX>(
+        p, mragged_tile_bound(R_cap, E_loc, CDA::BM, p.n_tiles), s);
   return run_gemm<CDA, false, B_KOUT, EPI_DA>(
       p, mragged_tile_bound(R_cap, E_loc, CDA::BM, p.n_tiles), s);
 }

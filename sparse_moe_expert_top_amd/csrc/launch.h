@@ -41,15 +41,22 @@ hipError_t launch_gemm_gate_up(const uint16_t* x, const int32_t* row_token,
                                const int32_t* offsets, int E_loc, int64_t R_cap, int d, int H,
                                const uint16_t* w_gu, SituCoef c, uint16_t* h, uint16_t* a,
                                hipStream_t s);
+// gate_up storing the saved h as MXFP8 (codes [R, 2H], scale bytes [R, 2H/32]).
+hipError_t launch_gemm_gate_up_mx(const uint16_t* x, const int32_t* row_token,
+                                  const int32_t* offsets, int E_loc, int64_t R_cap, int d,
+                                  int H, const uint16_t* w_gu, SituCoef c, uint8_t* h_codes,
+                                  uint8_t* h_scales, uint16_t* a, hipStream_t s);
 hipError_t launch_gemm_down(const uint16_t* a, const int32_t* offsets, const float* row_gate,
                             int E_loc, int64_t R_cap, int H, int d, const uint16_t* w_down,
                             uint16_t* rows_out, hipStream_t s);
 // dA: G = dy[row_token] . w_down[e]; epilogue writes dh, pa = bf16(p a) and dp partials.
 int gemm_da_slots(int H);
+// The saved h is read from bf16 `h`, or from MXFP8 codes and scales when h_codes != nullptr.
 hipError_t launch_gemm_da(const uint16_t* dy, const int32_t* row_token, const int32_t* offsets,
                           int E_loc, int64_t R_cap, int d, int H, const uint16_t* w_down,
-                          const uint16_t* h, const float* row_gate, SituCoef c, uint16_t* dh,
-                          uint16_t* pa, float* dp_part, hipStream_t s);
+                          const uint16_t* h, const uint8_t* h_codes, const uint8_t* h_scales,
+                          const float* row_gate, SituCoef c, uint16_t* dh, uint16_t* pa,
+                          float* dp_part, hipStream_t s);
 // dX rows: dh . w_gu[e]  ->  bf16 rows [R, d]
 hipError_t launch_gemm_dx(const uint16_t* dh, const int32_t* offsets, int E_loc,
                           int64_t R_cap, int d, int H, const uint16_t* w_gu,
@@ -61,5 +68,11 @@ hipError_t launch_gemm_dw_down(const uint16_t* dy, const int32_t* row_token,
 hipError_t launch_gemm_dw_gu(const uint16_t* dh, const uint16_t* x, const int32_t* row_token,
                              const int32_t* offsets, int E_loc, int d, int H, float* dw_gu,
                              hipStream_t s);
+
+// MXFP8 storage format of the saved pre-activation (mxfp8.h); n a multiple of 32.
+hipError_t launch_mx_quantize(const uint16_t* v, int64_t rows, int n, uint8_t* codes,
+                              uint8_t* scales, hipStream_t s);
+hipError_t launch_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int n,
+                                uint16_t* out, hipStream_t s);
 
 }  // namespace moe

@@ -1,0 +1,90 @@
+// MXFP8 storage of the saved pre-activation, shared by the GEMM epilogues and the standalone
+// quantizer.
+//
+// "Kimi K3 ... Memory" (unified activation manager; ledger summary) keeps most saved
+// activations block-wise in FP8, which halves them again. The pages do not fix the format;
+// this library reads it as OCP Microscaling v1.0 MXFP8:
+//   * E4M3 elements: 1 sign, 4 exponent bits (bias 7), 3 mantissa bits, no infinities,
+//     largest finite 448, subnormal quantum 2^-9. Encoding rounds to nearest, ties to even,
+//     saturates to +-448, and keeps the sign of values that round to zero.
+//   * 32 consecutive elements of a row share a scale 2^X, stored as the byte X + 127, with
+//     X = floor(log2(amax)) - 8 clamped to [-127, 127] (-127 for an all-zero block).
+// A stored row of n elements is n code bytes plus n/32 scale bytes (1.03 bytes per element
+// against 2 for bf16). Encoding works on the fp32 bits (no hardware conversion), so its
+// result does not depend on a conversion instruction's rounding or saturation mode.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+constexpr int kMxBlock = 32;
+
+// E8M0 scale byte of a block from its largest magnitude (a finite, non-negative fp32).
+__device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
+  // biased fp32 exponent = floor(log2(amax)) + 127 for normal amax; 0 for zero or subnormal,
+  // whose true X lies below the clamp anyway
+  const int ex = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
+  int X = ex - 127 - 8;
+  X = X < -127 ? -127 : (X > 127 ? 127 : X);
+  return (uint32_t)(X + 127);
+}
+
+// E4M3 code of a finite fp32 value (the element already divided by its block scale).
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t au = u & 0x7FFFFFFFu;
+  const float a = __uint_as_float(au);
+  uint32_t mag;
+  if (a >= 448.0f) {
+    mag = 0x7Eu;                                   // saturate
+  } else if (a < 0.015625f) {                      // below 2^-6: quantum 2^-9, codes 0..8
+    mag = (uint32_t)__builtin_rintf(a * 512.0f);   // exact scaling; rint ties to even
+  } else {
+    const uint32_t q = (((au >> 23) - 120u) << 3) | ((au >> 20) & 7u);   // exponent bias 7
+    const uint32_t rem = au & 0xFFFFFu;            // the 20 mantissa bits that are dropped
+    const uint32_t up = (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ? 1u : 0u;
+    mag = q + up;                                  // a carry moves to the next binade
+    mag = mag > 0x7Eu ? 0x7Eu : mag;
+  }
+  return sign | mag;
+}
+
+// Value of an E4M3 code (the encoder never produces the NaN codes).
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  const uint32_t ex = (c >> 3) & 0xFu, m = c & 7u;
+  const float mag = ex ? __uint_as_float(((ex + 120u) << 23) | (m << 20))
+                       : (float)m * 0.001953125f;
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// 8 consecutive elements of one block: codes packed little-endian into two words.
+__device__ __forceinline__ u32x2 mx_encode8(const float (&v)[8], uint32_t scale_byte) {
+  const int nx = 127 - (int)scale_byte;            // -X
+  u32x2 out;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      word |= e4m3_encode(__builtin_amdgcn_ldexpf(v[4 * w + b], nx)) << (8 * b);
+    out[w] = word;
+  }
+  return out;
+}
+__device__ __forceinline__ void mx_decode8(u32x2 codes, uint32_t scale_byte, float (&v)[8]) {
+  const int X = (int)scale_byte - 127;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    v[i] = __builtin_amdgcn_ldexpf(e4m3_decode((codes[i >> 2] >> (8 * (i & 3))) & 0xFFu), X);
+}
+
+// Largest magnitude over the 4 lanes (xor 1, 2) that hold one 32-element block.
+__device__ __forceinline__ float mx_amax4(float m) {
+  m = fmaxf(m, __shfl_xor(m, 1, 64));
+  m = fmaxf(m, __shfl_xor(m, 2, 64));
+  return m;
+}
+
+}  // namespace moe

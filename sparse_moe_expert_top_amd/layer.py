@@ -7,6 +7,9 @@ Saved for the backward: the pre-dispatch input x, the bf16 pre-activation h [R, 
 routing metadata; a and o are not kept ("Frontier-scale RL with Kimi K3", "Streaming
 activations": only the bf16 input of the activation is saved).
 Backward: moe_expert_bwd (re-dispatch, dA + SiTU-GLU' + dp, dW_down, dW_gu, dX, combine).
+With h_store="mxfp8" the saved h is kept block-wise in FP8 instead ("Kimi K3 ... Memory",
+unified activation manager: most saved activations are block-wise FP8), through
+moe_grouped_gemm_gate_up_mx and moe_expert_bwd_mx.
 
 `LayerBuffers` allocates every buffer once (torch, HBM) so a training step issues only the
 library's kernels; buffers indexed by routed rows are sized by a capacity R_cap (T*k by
@@ -37,9 +40,13 @@ class LayerShape:
 class LayerBuffers:
     """Device buffers for one layer call of a given shape, reused across steps."""
 
-    def __init__(self, shape: LayerShape, R_cap: int | None = None, device="cuda"):
+    def __init__(self, shape: LayerShape, R_cap: int | None = None, device="cuda",
+                 h_store: str = "bf16"):
+        if h_store not in ("bf16", "mxfp8"):
+            raise ValueError(f"h_store must be 'bf16' or 'mxfp8', not {h_store!r}")
         s = shape
         self.shape = s
+        self.h_store = h_store
         self.R_cap = s.T * s.k if R_cap is None else int(R_cap)
         R = max(self.R_cap, 1)
         i32, f32, bf = torch.int32, torch.float32, torch.bfloat16
@@ -50,7 +57,12 @@ class LayerBuffers:
                          row_gate=e(R, dt=f32), slot_row=e(s.T, s.k, dt=i32),
                          status=e(1, dt=i32))
         self.ws_perm = e(max(_lib.workspace_size(_lib.MOE_WS_PERMUTE, T=s.T, E_loc=s.E_loc), 256), dt=torch.uint8)
-        self.h = e(R, 2 * s.H, dt=bf)
+        if h_store == "mxfp8":
+            self.h = None
+            self.h_codes = e(R, 2 * s.H, dt=torch.uint8)
+            self.h_scales = e(R, 2 * s.H // 32, dt=torch.uint8)
+        else:
+            self.h = e(R, 2 * s.H, dt=bf)
         self.a = e(R, s.H, dt=bf)
         self.y = e(s.T, s.d, dt=bf)
         self.ws_down = e(max(_lib.workspace_size(_lib.MOE_WS_DOWN_COMBINE, T=s.T, E_loc=s.E_loc,
@@ -74,8 +86,14 @@ class LayerBuffers:
     def forward(self, x, logits, w_gu, w_down):
         s = self.shape
         self.route(logits)
-        _lib.moe_grouped_gemm_gate_up(x, self.perm["row_token"], self.perm["offsets"], w_gu,
-                                      self.R_cap, s.beta, s.linear_beta, h=self.h, a=self.a)
+        if self.h_store == "mxfp8":
+            _lib.moe_grouped_gemm_gate_up_mx(x, self.perm["row_token"], self.perm["offsets"],
+                                             w_gu, self.R_cap, s.beta, s.linear_beta,
+                                             h_codes=self.h_codes, h_scales=self.h_scales,
+                                             a=self.a)
+        else:
+            _lib.moe_grouped_gemm_gate_up(x, self.perm["row_token"], self.perm["offsets"], w_gu,
+                                          self.R_cap, s.beta, s.linear_beta, h=self.h, a=self.a)
         _lib.moe_grouped_gemm_down_combine(self.a, self.perm["offsets"], self.perm["row_gate"],
                                            self.perm["slot_row"], w_down, self.R_cap, y=self.y,
                                            ws=self.ws_down)
@@ -83,9 +101,15 @@ class LayerBuffers:
 
     def backward(self, dy, x, w_gu, w_down):
         s = self.shape
-        _lib.moe_expert_bwd(dy, x, self.h, self.perm, w_gu, w_down, self.R_cap, s.beta,
-                            s.linear_beta, dx=self.dx, dw_gu=self.dw_gu, dw_down=self.dw_down,
-                            dp=self.dp, ws=self.ws_bwd)
+        if self.h_store == "mxfp8":
+            _lib.moe_expert_bwd_mx(dy, x, self.h_codes, self.h_scales, self.perm, w_gu, w_down,
+                                   self.R_cap, s.beta, s.linear_beta, dx=self.dx,
+                                   dw_gu=self.dw_gu, dw_down=self.dw_down, dp=self.dp,
+                                   ws=self.ws_bwd)
+        else:
+            _lib.moe_expert_bwd(dy, x, self.h, self.perm, w_gu, w_down, self.R_cap, s.beta,
+                                s.linear_beta, dx=self.dx, dw_gu=self.dw_gu,
+                                dw_down=self.dw_down, dp=self.dp, ws=self.ws_bwd)
         return self.dx, self.dw_gu, self.dw_down, self.dp
 
     def step(self, x, logits, w_gu, w_down, dy):

@@ -407,3 +407,74 @@ def compare_sampled(m, cfg, n_tok=48, n_exp=3, n_col=6, seed=0):
 def test_layer_full_size_sampled(moe, name):
     compare_sampled(moe, LAYER_CONFIGS[name])
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ MXFP8 storage of the saved h
+def test_mxfp8_quantize_dequantize(moe):
+    """The standalone quantizer is bit-exact with the oracle's MXFP8 (codes and scale bytes)
+    and the dequantizer returns the stored values exactly."""
+    from moe_inputs import f32_to_bf16_bits
+    rng = np.random.default_rng(11)
+    rows, n = 300, 256
+    v = rng.standard_normal((rows, n)).astype(np.float32)
+    v *= np.exp(rng.uniform(-30, 30, size=(rows, 1))).astype(np.float32)
+    v[0, :32] = 0.0                                      # all-zero block
+    v[1, :32] = -0.0                                     # negative zeros
+    v[2, 5] = 1e4                                        # one outlier: the rest of the block is small
+    v[3, ::7] *= 600.0                                   # several values in the saturation band
+    v[4, :64] = rng.standard_normal(64).astype(np.float32) * 1e-38   # subnormal fp32 range
+    vb = f32_to_bf16_bits(v)
+    codes, scales = moe.moe_mxfp8_quantize(dev_bf16(vb))
+    back = moe.moe_mxfp8_dequantize(codes, scales)
+    torch.cuda.synchronize()
+    ref_c, ref_s = oracle.mxfp8.quantize(oracle.bf16_widen(vb))
+    assert np.array_equal(scales.cpu().numpy(), ref_s)
+    assert np.array_equal(codes.cpu().numpy(), ref_c)
+    ref_v = oracle.mxfp8.dequantize(ref_c, ref_s)
+    got_v = host_bf16(back)
+    big = np.abs(ref_v) >= 2.0 ** -126
+    assert np.array_equal(got_v[big], ref_v[big])
+    assert np.all(np.abs(got_v[~big] - ref_v[~big]) <= 2.0 ** -126)
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid"])
+def test_layer_mxfp8_store(moe, name):
+    """Layer with the saved h stored as MXFP8: the stored codes and scales equal the oracle's
+    MXFP8 of its bf16 h (dyadic inputs make h exact on both sides); the forward is bit-identical
+    to the bf16-store path; the backward matches the oracle recomputing from the stored h."""
+    from moe_inputs import dyadic_layer_inputs
+    cfg = SMALL_CASES[name]
+    say(f"layer mxfp8 {name}")
+    inp = dyadic_layer_inputs(cfg, seed=0)
+    idx, gates, perm = oracle_route_perm(inp, cfg)
+    shape = moe.LayerShape(T=cfg.T, E=cfg.E, k=cfg.k, e_lo=cfg.e_lo, E_loc=cfg.E_loc, d=cfg.d,
+                           H=cfg.H, beta=cfg.beta, linear_beta=cfg.linear_beta)
+    t = dict(x=dev_bf16(inp["x"]), logits=dev(inp["logits"]), w_gu=dev_bf16(inp["w_gu"]),
+             w_down=dev_bf16(inp["w_down"]), dy=dev_bf16(inp["dy"]))
+    buf = moe.LayerBuffers(shape, h_store="mxfp8")
+    buf.step(t["x"], t["logits"], t["w_gu"], t["w_down"], t["dy"])
+    ref16 = moe.LayerBuffers(shape)
+    ref16.forward(t["x"], t["logits"], t["w_gu"], t["w_down"])
+    torch.cuda.synchronize()
+    check_route_perm(buf, idx, gates, perm)
+    R = perm["R"]
+    f = oracle.expert_layer_fwd(inp["x"], inp["w_gu"], inp["w_down"], perm, cfg.H, mode="S")
+    assert np.array_equal(host_bf16(ref16.h[:R]), f["h"])          # h is exact on both sides
+    ref_c, ref_s = oracle.mxfp8.quantize(f["h"])
+    assert np.array_equal(buf.h_codes[:R].cpu().numpy(), ref_c)
+    assert np.array_equal(buf.h_scales[:R].cpu().numpy(), ref_s)
+    assert torch.equal(buf.a[:R].view(torch.int16), ref16.a[:R].view(torch.int16))
+    assert torch.equal(buf.y.view(torch.int16), ref16.y.view(torch.int16))
+    b = oracle.expert_layer_bwd(inp["x"], inp["dy"], inp["w_gu"], inp["w_down"], perm, cfg.H,
+                                mode="S", h_store="mxfp8")
+    errs = dict(dx=rel_err(host_bf16(buf.dx), b["dx"]),
+                dw_gu=rel_err(buf.dw_gu.cpu().numpy(), b["dw_gu"]),
+                dw_down=rel_err(buf.dw_down.cpu().numpy(), b["dw_down"]),
+                dp=rel_err(buf.dp.cpu().numpy(), b["dp"]))
+    say(name, "R", R, {k: f"{v:.2e}" for k, v in errs.items()})
+    for k_, v in errs.items():
+        assert v <= (FP32_TOL if k_ == "dp" else BF16_TOL), (k_, v)
+    # the stored form matters: the oracle's bf16-store backward differs from the MXFP8 one
+    b16 = oracle.expert_layer_bwd(inp["x"], inp["dy"], inp["w_gu"], inp["w_down"], perm, cfg.H,
+                                  mode="S")
+    assert rel_err(b16["dp"], b["dp"]) > FP32_TOL
