@@ -46,11 +46,11 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def run_layer(m, cfg, inp, R_cap=None):
+def run_layer(m, cfg, inp, R_cap=None, h_store="bf16"):
     """Forward + backward through LayerBuffers (the benchmark's launch configuration)."""
     shape = m.LayerShape(T=inp["x"].shape[0], E=cfg.E, k=cfg.k, e_lo=cfg.e_lo, E_loc=cfg.E_loc,
                          d=cfg.d, H=cfg.H, beta=cfg.beta, linear_beta=cfg.linear_beta)
-    buf = m.LayerBuffers(shape, R_cap=R_cap)
+    buf = m.LayerBuffers(shape, R_cap=R_cap, h_store=h_store)
     t = dict(x=dev_bf16(inp["x"]), logits=dev(inp["logits"]), w_gu=dev_bf16(inp["w_gu"]),
              w_down=dev_bf16(inp["w_down"]), dy=dev_bf16(inp["dy"]))
     buf.step(t["x"], t["logits"], t["w_gu"], t["w_down"], t["dy"])
@@ -340,13 +340,21 @@ def test_layer_token_permutation(moe):
 
 
 # ------------------------------------------------------------------------------- layer, full-size sampled
-def compare_sampled(m, cfg, n_tok=48, n_exp=3, n_col=6, seed=0):
-    say(f"layer sampled {cfg.name}: generating inputs")
-    inp = layer_inputs(cfg, seed=0)
+def compare_sampled(m, cfg, n_tok=48, n_exp=3, n_col=6, seed=0, h_store="bf16"):
+    """Sampled comparison at full size. h_store="mxfp8" runs the MXFP8-store path on dyadic
+    inputs (h exact on both sides), checks the stored codes and scales of the sampled rows bit
+    for bit and takes weight-gradient columns in whole 32-column blocks."""
+    mx = h_store == "mxfp8"
+    say(f"layer sampled {cfg.name} ({h_store}): generating inputs")
+    if mx:
+        from moe_inputs import dyadic_layer_inputs
+        inp = dyadic_layer_inputs(cfg, seed=0)
+    else:
+        inp = layer_inputs(cfg, seed=0)
     say(f"layer sampled {cfg.name}: oracle routing")
     idx, gates, perm = oracle_route_perm(inp, cfg)
     say(f"layer sampled {cfg.name}: GPU step (R={perm['R']})")
-    buf, t = run_layer(m, cfg, inp)
+    buf, t = run_layer(m, cfg, inp, h_store=h_store)
     check_route_perm(buf, idx, gates, perm)
     rng = np.random.default_rng(seed)
     local_tok = np.unique(perm["row_token"]) if perm["R"] else np.zeros(0, int)
@@ -356,7 +364,7 @@ def compare_sampled(m, cfg, n_tok=48, n_exp=3, n_col=6, seed=0):
     say(f"layer sampled {cfg.name}: oracle on {len(rows)} rows")
     f = oracle.expert_layer_fwd(inp["x"], inp["w_gu"], inp["w_down"], sub, cfg.H, mode="S")
     b = oracle.expert_layer_bwd(inp["x"], inp["dy"], inp["w_gu"], inp["w_down"], sub, cfg.H,
-                                mode="S")
+                                mode="S", h_store=h_store)
     toks = np.unique(toks)
     tt = torch.from_numpy(toks).cuda()
     rr = torch.from_numpy(rows).cuda()
@@ -364,15 +372,25 @@ def compare_sampled(m, cfg, n_tok=48, n_exp=3, n_col=6, seed=0):
         y=rel_err(host_bf16(buf.y[tt]), f["y"][toks]),
         dx=rel_err(host_bf16(buf.dx[tt]), b["dx"][toks]),
         dp=rel_err(buf.dp[tt].cpu().numpy(), b["dp"][toks]),
-        h=rel_err(host_bf16(buf.h[rr]), f["h"]),
         a=rel_err(host_bf16(buf.a[rr]), f["a"]),
     )
+    if mx:
+        ref_c, ref_s = oracle.mxfp8.quantize(f["h"])
+        assert np.array_equal(buf.h_codes[rr].cpu().numpy(), ref_c)
+        assert np.array_equal(buf.h_scales[rr].cpu().numpy(), ref_s)
+    else:
+        errs["h"] = rel_err(host_bf16(buf.h[rr]), f["h"])
     # weight gradients: sampled experts x intermediate columns (all rows of the expert)
     counts = np.diff(perm["offsets"])
     exps = list(rng.choice(cfg.E_loc, n_exp, replace=False))
     if np.any(counts == 0):
         exps.append(int(np.nonzero(counts == 0)[0][0]))
-    cols = np.unique(np.concatenate([rng.choice(cfg.H, n_col, replace=False), [0, cfg.H - 1]]))
+    if mx:
+        nb = cfg.H // 32
+        blk = np.unique(np.concatenate([rng.choice(nb, 2, replace=False), [0, nb - 1]]))
+        cols = (blk[:, None] * 32 + np.arange(32)[None, :]).reshape(-1)
+    else:
+        cols = np.unique(np.concatenate([rng.choice(cfg.H, n_col, replace=False), [0, cfg.H - 1]]))
     dwg = buf.dw_gu
     dwd = buf.dw_down
     e_gu, e_dn = [], []
@@ -380,7 +398,7 @@ def compare_sampled(m, cfg, n_tok=48, n_exp=3, n_col=6, seed=0):
     for e in exps:
         say(f"layer sampled {cfg.name}: dW expert {e} rows {counts[e]}")
         gu, dn = oracle.dw_columns(inp["x"], inp["dy"], inp["w_gu"], inp["w_down"], perm, int(e),
-                                   cols, cfg.H)
+                                   cols, cfg.H, h_store=h_store)
         ci = torch.from_numpy(np.concatenate([cols, cfg.H + cols])).cuda()
         got_gu_all.append(dwg[int(e)][ci].cpu().numpy())
         got_dn_all.append(dwd[int(e)][:, torch.from_numpy(cols).cuda()].cpu().numpy())
@@ -406,6 +424,12 @@ def compare_sampled(m, cfg, n_tok=48, n_exp=3, n_col=6, seed=0):
 @pytest.mark.parametrize("name", ["shard", "skew", "skew_mid", "skew_tail", "large"])
 def test_layer_full_size_sampled(moe, name):
     compare_sampled(moe, LAYER_CONFIGS[name])
+    torch.cuda.empty_cache()
+
+
+def test_layer_mxfp8_full_size_sampled(moe):
+    """The MXFP8-store path at the shard workload's full size."""
+    compare_sampled(moe, LAYER_CONFIGS["shard"], h_store="mxfp8")
     torch.cuda.empty_cache()
 
 
