@@ -244,13 +244,31 @@ def main():
         "saved_activation_GB": round((R * 2 * cfg.H * 2 + cfg.T * cfg.d * 2) / 1e9, 3),
         "naive_saved_fp32_GB": round(6 * R * cfg.H * 4 / 1e9, 3),
     }
+    # the same step with the saved h stored as MXFP8 (E4M3 codes + one scale byte per 32)
+    del buf
+    torch.cuda.empty_cache()
+    bmx = moe.LayerBuffers(shape, h_store="mxfp8")
+    for _ in range(args.warmup):
+        bmx.step(x, logits, w_gu, w_down, dy)
+    torch.cuda.synchronize()
+    n_mx = max(1, args.steps // 2)
+    t0 = time.perf_counter()
+    for _ in range(n_mx):
+        bmx.step(x, logits, w_gu, w_down, dy)
+    torch.cuda.synchronize()
+    ms_mx = (time.perf_counter() - t0) * 1e3 / n_mx
+    out["mxfp8_h"] = {"ms_per_step": round(ms_mx, 4),
+                      "value": round(flop_step / (ms_mx * 1e-3) / 1e12, 2),
+                      "saved_activation_GB": round((R * 2 * cfg.H * (1 + 1 / 32) + cfg.T * cfg.d * 2) / 1e9, 3),
+                      "steps": n_mx}
+    del bmx
+    torch.cuda.empty_cache()
+
     tr = committed_traffic(args.workload)
     if tr is not None:
         out["roofline"]["traffic"] = tr["fetch"] + tr["write"]
         out["roofline"].update(traffic_fetch_bytes=tr["fetch"], traffic_write_bytes=tr["write"],
                                traffic_vs_algorithmic=round((tr["fetch"] + tr["write"]) / gu_bytes, 3))
-    del buf
-    torch.cuda.empty_cache()
 
     if not args.no_situ:
         sc = SITU_CONFIGS["situ"]
