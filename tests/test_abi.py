@@ -107,3 +107,36 @@ def test_expert_bwd_rejects(lib):
     assert lib.moe_expert_bwd(*a) == ENULL
     a = list(base); a[8] = 0
     assert lib.moe_expert_bwd(*a) == ESHAPE
+
+
+def test_mxfp8_entry_points_reject(lib):
+    P = ctypes.c_void_p(256)
+    U = ctypes.c_void_p(264)                                           # 8- but not 16-byte aligned
+    # standalone quantizer / dequantizer
+    assert lib.moe_mxfp8_quantize(P, 10, 48, P, P, None) == EUNSUP    # n % 32
+    assert lib.moe_mxfp8_quantize(P, -1, 64, P, P, None) == ESHAPE
+    assert lib.moe_mxfp8_quantize(P, 10, 64, P, None, None) == ENULL
+    assert lib.moe_mxfp8_quantize(P, 10, 64, U, P, None) == EUNSUP    # codes alignment
+    assert lib.moe_mxfp8_quantize(None, 0, 64, None, None, None) == OK
+    assert lib.moe_mxfp8_dequantize(P, P, 10, 40, P, None) == EUNSUP
+    assert lib.moe_mxfp8_dequantize(P, None, 10, 64, P, None) == ENULL
+    assert lib.moe_mxfp8_dequantize(P, P, 0, 64, None, None) == OK
+    # gate/up writing MXFP8 h
+    gu = lib.moe_grouped_gemm_gate_up_mx
+    assert gu(P, P, P, 4, 100, 100, 64, P, 4.0, 25.0, P, P, P, None) == EUNSUP   # d % 64
+    assert gu(P, P, P, 4, 100, 128, 64, P, 4.0, 25.0, P, None, P, None) == ENULL # scales
+    assert gu(P, P, P, 4, 100, 128, 64, P, 4.0, 25.0, U, P, P, None) == EUNSUP   # codes alignment
+    assert gu(P, P, P, 4, 100, 128, 64, P, 4.0, 0.0, P, P, P, None) == ESHAPE    # linear_beta
+    assert gu(P, None, P, 4, 0, 128, 64, P, 4.0, 25.0, None, None, None, None) == OK   # R_cap = 0
+    # backward reading MXFP8 h
+    base = [P, P, P, P, P, P, P, P, 8, 2, 4, 16, 128, 64, P, P, 4.0, 25.0, P, P, P, P, P,
+            1 << 30, None]
+    bw = lib.moe_expert_bwd_mx
+    a = list(base); a[23] = 10
+    assert bw(*a) == EWS
+    a = list(base); a[3] = None                                        # h_scales
+    assert bw(*a) == ENULL
+    a = list(base); a[12] = 96
+    assert bw(*a) == EUNSUP
+    a = list(base); a[9] = 0
+    assert bw(*a) == ESHAPE
