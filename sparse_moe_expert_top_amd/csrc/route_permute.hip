@@ -287,8 +287,9 @@ hipError_t launch_permute(const int32_t* idx, const float* gates, int64_t T, int
 
 // ------------------------------------------------------------------------------ combine
 // out[t] = bf16( sum_j w(r) rows[r] ), r = slot_row[t, j] >= 0, in fp32 and slot order.
-// One workgroup per token at a time; each lane owns 8 consecutive columns (16 bytes).
-__global__ __launch_bounds__(256) void unpermute_kernel(const uint16_t* __restrict__ rows,
+// One workgroup per token at a time, sized to the row (one lane per 8 consecutive columns,
+// 16 bytes, up to 1024 lanes); the output row is written with streaming stores.
+__global__ __launch_bounds__(1024) void unpermute_kernel(const uint16_t* __restrict__ rows,
                                                         const int32_t* __restrict__ slot_row,
                                                         const float* __restrict__ w,
                                                         int64_t T, int k, int n,
@@ -314,7 +315,7 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const uint16_t* __restri
       u32x4 o;
 #pragma unroll
       for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
-      *(u32x4*)(out + t * n + 8 * c) = o;
+      __builtin_nontemporal_store(o, (u32x4*)(out + t * n + 8 * c));
     }
   }
 }
@@ -322,11 +323,13 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const uint16_t* __restri
 hipError_t launch_unpermute(const uint16_t* rows, const int32_t* slot_row, const float* w,
                             int64_t T, int k, int n, uint16_t* out, hipStream_t s) {
   if (T == 0 || n == 0) return hipSuccess;
+  const int nc = n / 8;
+  const int threads = nc >= 1024 ? 1024 : ((nc + 63) / 64) * 64;
   int64_t blocks = T;
-  const int64_t cap = (int64_t)device_cu_count() * 16;
+  const int64_t cap = (int64_t)device_cu_count() * (16 * 256 / threads + 1);
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL(unpermute_kernel, dim3((unsigned)blocks), dim3(256), 0, s, rows, slot_row,
-                     w, T, k, n, out);
+  hipLaunchKernelGGL(unpermute_kernel, dim3((unsigned)blocks), dim3(threads), 0, s, rows,
+                     slot_row, w, T, k, n, out);
   return hipGetLastError();
 }
 
