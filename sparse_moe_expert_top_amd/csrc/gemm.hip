@@ -428,7 +428,18 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
     const int Mg = KRAG ? p.M : gcount;
     const int Kg = KRAG ? gcount : p.K;
     const int nk = (Kg + BK - 1) / BK;
-    const int m0 = mt * BM;
+    int m0 = mt * BM;
+    int Me = Mg;                           // end (exclusive) of this tile's rows
+    if constexpr (!KRAG) {
+      // A group's 32-row fragments are dealt out evenly over its m-tiles (588 rows: 7, 6 and 6
+      // fragments, not 8, 8 and 3), so the m-tiles that share an expert's weight panel do
+      // nearly equal MFMA work and stay in step over the k-loop; a short last tile would run
+      // ahead and lose the panel's L2 lines before its siblings read them.
+      const int nm = (Mg + BM - 1) / BM;
+      const int F = (Mg + 31) / 32;
+      m0 = 32 * ((mt * F) / nm);
+      Me = min(32 * (((mt + 1) * F) / nm), Mg);
+    }
     const int n0 = nt * BN;
     const int j0 = nt * (BN / 2);          // gate_up: first gate/linear column pair
     const uint16_t* Bg = p.B + (int64_t)g * p.b_gstride;
@@ -458,7 +469,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
       if constexpr (!A_KO) {
         const int row = byte / (BK * 2);
         const int c = ((byte % (BK * 2)) >> 4) ^ rswz<BK>(row);
-        const int m = min(m0 + row, Mg - 1);
+        const int m = min(m0 + row, Me - 1);
         const int srow = p.a_gather ? p.a_gather[r0 + m] : m;
         a_off[q] = (uint32_t)(((int64_t)srow * p.lda + c * 8) * 2);
       } else {
@@ -680,7 +691,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
     int nfv = FM;
     if constexpr (!KRAG) {
       const int wrow0 = m0 + (wave_u / C::WGN) * WM;
-      nfv = max(0, min(FM, (Mg - wrow0 + 31) / 32));
+      nfv = max(0, min(FM, (Me - wrow0 + 31) / 32));
     }
     nfv = __builtin_amdgcn_readfirstlane(nfv);
     if constexpr (KRAG) kloop(std::integral_constant<int, FM>{});
@@ -756,7 +767,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
           const f32x4 g1 = *(const f32x4*)&st[row * EPS + cc * 8 + 4];
           const f32x4 l0 = *(const f32x4*)&st[row * EPS + 32 + cc * 8];
           const f32x4 l1 = *(const f32x4*)&st[row * EPS + 32 + cc * 8 + 4];
-          if (rblk + row < Mg && jj < p.H) {
+          if (rblk + row < Me && jj < p.H) {
             const int64_t r = r0 + rblk + row;
             const float gv[8] = {g0[0], g0[1], g0[2], g0[3], g1[0], g1[1], g1[2], g1[3]};
             const float lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
@@ -814,7 +825,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
           const f32x4 c1 = *(const f32x4*)&st[row * EPS + cc * 8 + 4];
           const float cv[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
           if constexpr (EPI == EPI_ROWS || EPI == EPI_ROWS_SCALED) {
-            if (rblk + row < Mg && col < p.N) {
+            if (rblk + row < Me && col < p.N) {
               const int64_t r = r0 + rblk + row;
               float sc = 1.0f;
               if constexpr (EPI == EPI_ROWS_SCALED) sc = p.row_scale[r];
@@ -824,7 +835,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
               st_row16(&p.o0[r * p.ld0 + col], o);
             }
           } else if constexpr (IS_DA) {
-            if (rblk + row < Mg && col < p.N) {
+            if (rblk + row < Me && col < p.N) {
               const int64_t r = r0 + rblk + row;
               const float pr = p.row_scale[r];
               // the saved pre-activation of these 8 columns (gate half, linear half): bf16
@@ -891,7 +902,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
             v += __shfl_xor(v, 2, 64);
             v += __shfl_xor(v, 4, 64);
             const int row = ps * 8 + (lane >> 3);
-            if (cc == 0 && rblk + row < Mg) p.dp_part[(int64_t)slot * p.dp_ld + r0 + rblk + row] = v;
+            if (cc == 0 && rblk + row < Me) p.dp_part[(int64_t)slot * p.dp_ld + r0 + rblk + row] = v;
           }
         }
       }
