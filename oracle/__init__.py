@@ -20,6 +20,10 @@ What it computes, and where the pages define it:
     activation manager; ledger summary): saved activations kept block-wise in FP8. Format
     read as OCP MX v1.0 MXFP8 (E4M3 elements, 32-element blocks, E8M0 scales); the layer
     backward takes h_store="mxfp8" to recompute from the stored value.
+  * W4A8 forward (`w4a8.expert_layer_fwd_w4a8`) with MXFP4 weights (`mxfp4`) - "Frontier-scale
+    RL with Kimi K3", "Low precision (MXFP4) rollouts": rollouts run the MoE layers with
+    4-bit weights and 8-bit activations. Formats read as OCP MX v1.0 MXFP4 (E2M1) and MXFP8
+    (E4M3), blocks of 32 along the reduction dimension.
 
 Two numeric modes:
   * "X" (exact): no intermediate rounding; used for the mathematical invariants.
@@ -34,6 +38,7 @@ from .bf16 import bf16_round, bf16_widen, bf16_to_bits
 from .situ import situ_glu_fwd, situ_glu_bwd, situ_parts
 from .route import route_topk
 from .permute import permute
+from . import mxfp4, mxfp8, w4a8
 from .layer import (expert_layer_fwd, expert_layer_bwd, token_layer_fwd, token_layer_bwd,
                     dw_columns, router_bwd, unpermute_sum)
 

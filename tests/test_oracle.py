@@ -543,3 +543,178 @@ def test_mx_layer_bwd_reduces_to_bf16_store_on_representable_h():
     for key in ("dx", "dw_gu", "dw_down", "dp"):
         e = np.max(np.abs(g2[key] - r2[key])) / np.max(np.abs(r2[key]))
         assert 0 < e < 0.1, (key, e)
+
+
+# ------------------------------------------------------------------ W4A8 (MXFP4 weights)
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]     # OCP MX v1.0, FP4 E2M1 magnitudes
+
+
+def _e2m1_nearest(v):
+    """Brute force: the E2M1 code nearest to v (|v| capped at 6), ties to the even code."""
+    a = min(abs(v), 6.0)
+    best = min(range(8), key=lambda c: (abs(a - E2M1_TABLE[c]), c % 2))
+    return best | (8 if math.copysign(1.0, v) < 0 else 0)
+
+
+def _e4m3_nearest(v):
+    """Brute force over the 127 finite E4M3 magnitudes, ties to the even code, saturating."""
+    mags = [(1 + (c & 7) / 8) * 2.0 ** ((c >> 3) - 7) if c >> 3 else (c & 7) * 2.0 ** -9
+            for c in range(127)]
+    a = min(abs(v), 448.0)
+    best = min(range(127), key=lambda c: (abs(a - mags[c]), c % 2))
+    return mags[best] * (-1.0 if math.copysign(1.0, v) < 0 else 1.0)
+
+
+def _mx_block_scalar(vals, emax, nearest_value):
+    """One MX block quantized with scalar loops: X from math.frexp of the largest magnitude."""
+    amax = max(abs(v) for v in vals)
+    X = -127 if amax == 0 else max(-127, min(127, math.frexp(amax)[1] - 1 - emax))
+    return [nearest_value(v / 2.0 ** X) * 2.0 ** X for v in vals]
+
+
+def test_mx4_e2m1_decode_table():
+    """The 16 codes decode to the format's table, sign in bit 3 (code 8 is -0)."""
+    from oracle import mxfp4
+    got = mxfp4.e2m1_decode(np.arange(16))
+    assert list(got[:8]) == E2M1_TABLE
+    assert list(got[8:]) == [-v for v in E2M1_TABLE]
+    assert math.copysign(1.0, got[8]) == -1.0
+
+
+def test_mx4_e2m1_encode_brute_force():
+    """Vectorised encoder = scalar brute force on every value, every midpoint, the
+    saturation band, signed zeros and random values."""
+    from oracle import mxfp4
+    tab = np.array(E2M1_TABLE)
+    mids = (tab[1:] + tab[:-1]) / 2
+    rng = np.random.default_rng(5)
+    x = np.concatenate([tab, -tab, mids, -mids, [6.5, 7.0, 7.99, 100.0, -9.0, 0.0, -0.0, -0.1],
+                        rng.uniform(-8, 8, 4000), rng.standard_normal(1000) * 0.3])
+    got = mxfp4.e2m1_encode(x)
+    ref = np.array([_e2m1_nearest(float(v)) for v in x], np.uint8)
+    assert np.array_equal(got, ref)
+    # ties to even: 0.25 -> 0, 0.75 -> 1.0, 1.25 -> 1.0, 1.75 -> 2.0, 2.5 -> 2, 3.5 -> 4, 5 -> 4
+    assert list(mxfp4.e2m1_decode(mxfp4.e2m1_encode(mids))) == [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0]
+
+
+def test_mx4_scale_exponent_rule():
+    """X = floor(log2 amax) - 2, clamped to [-127, 127]; zero blocks take -127."""
+    from oracle import mxfp4
+    amax = np.array([1.0, 4.0, 7.99, 8.0, 0.75, 0.0, 2.0 ** -130, 3e38, 2.0 ** -124])
+    assert list(mxfp4.block_scale_exp(amax)) == [-2, 0, 0, 1, -3, -127, -127, 125, -126]
+
+
+def test_mx4_packing_layout():
+    """Element 2j in the low nibble of byte j, 2j+1 in the high nibble; unpack inverts."""
+    from oracle import mxfp4
+    codes = np.array([[1, 2, 3, 4, 15, 0]], np.uint8)
+    assert list(mxfp4.pack(codes)[0]) == [0x21, 0x43, 0x0F]
+    assert np.array_equal(mxfp4.unpack(mxfp4.pack(codes)), codes)
+    v = np.zeros((1, 32))
+    v[0, 0], v[0, 1] = 6.0, -0.5                          # X = 0: codes 7 and 9
+    c, s = mxfp4.quantize(v)
+    assert c[0, 0] == 0x97 and s[0, 0] == 127 and np.all(c[0, 1:] == 0)
+
+
+def test_mx4_roundtrip_bounds():
+    """Per block the largest magnitude lands in [4, 8) times 2^X; elements above 6 * 2^X
+    saturate; the rest are within half a step (2^-2 relative at or above 2^X, 2^(X-2)
+    absolute below); representable blocks come back exactly."""
+    from oracle import mxfp4
+    rng = np.random.default_rng(6)
+    v = rng.standard_normal((64, 256)) * np.exp(rng.uniform(-20, 20, size=(64, 1)))
+    c, s = mxfp4.quantize(v)
+    d = mxfp4.dequantize(c, s)
+    X = (s.astype(np.int64) - 127).repeat(32, axis=1)
+    sc = np.ldexp(1.0, X)
+    amax = np.abs(v).reshape(64, 8, 32).max(-1).repeat(32, axis=1)
+    assert np.all((amax / sc >= 4) & (amax / sc < 8))
+    sat = np.abs(v) > 6 * sc
+    assert np.all(np.abs(d[sat]) == 6 * sc[sat])
+    ok = ~sat
+    err = np.abs(d - v)[ok]
+    assert np.all(err <= np.maximum(2.0 ** -2 * np.abs(v[ok]), 2.0 ** -2 * sc[ok]) * (1 + 1e-12))
+    exact = mxfp4.e2m1_decode(rng.integers(0, 16, size=(16, 64))) * 2.0 ** -3
+    exact[:, ::32] = 6.0 * 2.0 ** -3                     # fixes each block's scale at X = -3
+    assert np.array_equal(mxfp4.roundtrip(exact), exact)
+
+
+def test_w4a8_forward_brute_force_tiny():
+    """The W4A8 forward against scalar loops over tokens, slots, outputs and reductions,
+    with scalar MX quantizers written from the formats (brute-force nearest codes)."""
+    from oracle import w4a8
+    from oracle.situ import situ_glu_fwd
+    rng = np.random.default_rng(7)
+    T, d, H, E, k = 5, 64, 32, 3, 2
+    x = rng.standard_normal((T, d)) * 0.7
+    w_gu = rng.standard_normal((E, 2 * H, d)) * 0.2
+    w_down = rng.standard_normal((E, d, H)) * 0.2
+    idx = np.array([[0, 2], [1, 0], [2, 1], [0, 1], [2, 0]], np.int32)
+    gates = rng.uniform(0.2, 0.8, size=(T, k))
+    perm = oracle.permute(idx, gates, 0, E)
+    got = w4a8.expert_layer_fwd_w4a8(x, w_gu, w_down, perm, H)
+
+    def q8_row(row):
+        return sum((_mx_block_scalar(list(row[b:b + 32]), 8, _e4m3_nearest)
+                    for b in range(0, len(row), 32)), [])
+
+    def q4_row(row):
+        nearest = lambda v: math.copysign(E2M1_TABLE[_e2m1_nearest(v) & 7], 1.0) * (
+            -1.0 if _e2m1_nearest(v) & 8 else 1.0)
+        return sum((_mx_block_scalar(list(row[b:b + 32]), 2, nearest)
+                    for b in range(0, len(row), 32)), [])
+
+    y = np.zeros((T, d))
+    for t in range(T):
+        x8 = q8_row(x[t])
+        for j in range(k):
+            e = int(idx[t, j])
+            h = [sum(x8[c] * q4 for c, q4 in enumerate(q4_row(w_gu[e, n]))) for n in range(2 * H)]
+            h = bf16_round(np.array(h))
+            a = bf16_round(situ_glu_fwd(h[None, :], H)[0])
+            a8 = q8_row(a)
+            for n in range(d):
+                w4 = q4_row(w_down[e, n])
+                y[t, n] += gates[t, j] * sum(a8[c] * w4[c] for c in range(H))
+    assert np.allclose(got["y"], bf16_round(y), rtol=0, atol=1e-12 * np.max(np.abs(y)))
+
+
+def test_w4a8_lossless_inputs_reduce_to_bf16_layer():
+    """With x and the weights exactly representable in MXFP8 / MXFP4, the W4A8 forward has
+    the bf16 layer's h and a bit for bit, and its y differs from the bf16 layer's only by
+    the MXFP8 rounding of a: |dy| <= sum_e p sum_c |a8 - a| |w_down|, each |a8 - a| within
+    the E4M3 bound (half a step, or the clip to 448 * 2^X), plus one bf16 step of each y."""
+    from oracle import layer, mxfp4, mxfp8, w4a8
+    rng = np.random.default_rng(8)
+    T, d, H, E, k = 40, 64, 64, 4, 2
+    x = mxfp8.e4m3_decode(rng.integers(0, 127, size=(T, d)).astype(np.uint8)) * 2.0 ** -8
+    x *= np.where(rng.random(x.shape) < 0.5, -1.0, 1.0)
+    x[:, ::32] = 448 * 2.0 ** -8                          # every block's scale fixed: exact
+    w_gu = mxfp4.e2m1_decode(rng.integers(0, 16, size=(E, 2 * H, d))) * 2.0 ** -4
+    w_gu[:, :, ::32] = 6.0 * 2.0 ** -4
+    w_down = mxfp4.e2m1_decode(rng.integers(0, 16, size=(E, d, H))) * 2.0 ** -5
+    w_down[:, :, ::32] = -6.0 * 2.0 ** -5
+    assert np.array_equal(mxfp8.roundtrip(x), x) and np.array_equal(mxfp4.roundtrip(w_gu), w_gu)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    gates = rng.uniform(0.1, 0.9, size=(T, k))
+    perm = oracle.permute(idx, gates, 0, E)
+    got = w4a8.expert_layer_fwd_w4a8(x, w_gu, w_down, perm, H)
+    ref = layer.expert_layer_fwd(x, w_gu, w_down, perm, H, mode="S")
+    assert np.array_equal(got["h"], ref["h"]) and np.array_equal(got["a"], ref["a"])
+    a8 = mxfp8.dequantize(got["a_codes"], got["a_scales"])
+    X = (got["a_scales"].astype(np.int64) - 127).repeat(32, axis=1)
+    sc = np.ldexp(1.0, X)
+    sat = np.abs(ref["a"]) > 448 * sc                   # clipped to 448 * 2^X
+    step = np.where(sat, np.abs(ref["a"]) - 448 * sc,
+                    np.maximum(2.0 ** -4 * np.abs(ref["a"]), 2.0 ** -10 * sc))
+    assert np.all(np.abs(a8 - ref["a"]) <= step)
+    assert np.any(a8 != ref["a"])                          # a itself is generally not representable
+    bound = np.zeros((T, d))
+    off = perm["offsets"]
+    for e in range(E):
+        r0, r1 = off[e], off[e + 1]
+        bound[perm["row_token"][r0:r1]] += perm["row_gate"][r0:r1, None] * (
+            step[r0:r1] @ np.abs(w_down[e]).T)
+    dy = np.abs(got["y"] - ref["y"])
+    assert np.all(dy <= bound + 2.0 ** -7 * np.abs(ref["y"]) + 1e-30)
+    assert np.max(dy) > 0
