@@ -45,6 +45,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "gemm_util.h"
 #include "launch.h"
 #include "mxfp8.h"
 #include "situ_math.h"
@@ -126,13 +127,8 @@ __device__ __forceinline__ int kswz(int k) { return (k & 3) << 2; }
 // Source of k-rows past the end of a ragged K extent (must read as zeros).
 __device__ __attribute__((aligned(16))) uint16_t g_zero_row[256];
 
-// Direct-to-LDS loads (global_load_lds_dwordx4): each lane's 16 bytes land at LDS byte
-// address M0 + 16 * lane, M0 being wave-uniform. They are issued from inline assembly so the
-// compiler does not track them: its waitcnt pass cannot tell ring slots apart and would
-// otherwise drain every in-flight load before each LDS read. The kernel orders these loads
-// itself (explicit vmcnt waits plus barriers); M0 is saved and restored around them.
-//
-// dma_vaddr: one load from a per-lane 64-bit address.
+// dma_vaddr: one direct-to-LDS load (global_load_lds_dwordx4, issued and ordered like
+// dma_saddr) from a per-lane 64-bit address.
 __device__ __forceinline__ void dma_vaddr(const uint16_t* src, uint32_t lds_in) {
   const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(lds_in);
   uint32_t saved;
@@ -145,74 +141,6 @@ __device__ __forceinline__ void dma_vaddr(const uint16_t* src, uint32_t lds_in) 
       : "v"(src), "s"(lds_addr)
       : "memory");
 }
-// dma_saddr: L loads from a wave-uniform 64-bit base plus per-lane 32-bit byte offsets;
-// load q lands at lds0 + 1024 q.
-template <int L>
-__device__ __forceinline__ void dma_saddr(uint32_t lds0_in, const void* sbase,
-                                          const uint32_t (&voff)[L]) {
-  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds0_in);
-  uint32_t saved;
-  if constexpr (L == 1) {
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "global_load_lds_dwordx4 %3, %2\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "s"(lds0), "s"(sbase), "v"(voff[0])
-        : "memory");
-  } else if constexpr (L == 2) {
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "global_load_lds_dwordx4 %4, %3\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "global_load_lds_dwordx4 %5, %3\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "s"(lds0), "s"(lds0 + 1024u), "s"(sbase), "v"(voff[0]), "v"(voff[1])
-        : "memory");
-  } else if constexpr (L > 4) {
-    static_assert(L % 4 == 0, "loads per operand per stage");
-#pragma unroll
-    for (int h = 0; h < L / 4; ++h) {
-      const uint32_t part[4] = {voff[4 * h], voff[4 * h + 1], voff[4 * h + 2], voff[4 * h + 3]};
-      dma_saddr<4>(lds0 + 4096u * h, sbase, part);
-    }
-  } else {
-    static_assert(L == 4, "loads per operand per stage");
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %1\n\t"
-        "global_load_lds_dwordx4 %6, %5\n\t"
-        "s_mov_b32 m0, %2\n\t"
-        "global_load_lds_dwordx4 %7, %5\n\t"
-        "s_mov_b32 m0, %3\n\t"
-        "global_load_lds_dwordx4 %8, %5\n\t"
-        "s_mov_b32 m0, %4\n\t"
-        "global_load_lds_dwordx4 %9, %5\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "s"(lds0), "s"(lds0 + 1024u), "s"(lds0 + 2048u), "s"(lds0 + 3072u), "s"(sbase),
-          "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3])
-        : "memory");
-  }
-}
-__device__ __forceinline__ const void* uniform_ptr(const void* ptr) {
-  const uint64_t a = (uint64_t)(uintptr_t)ptr;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
-
-// Wait until at most N vector-memory operations of this wave are outstanding, and for all
-// of its LDS operations (gfx9 s_waitcnt: vmcnt[3:0,15:14], expcnt[6:4], lgkmcnt[11:8]).
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-  static_assert(N >= 0 && N < 64, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((N >> 4) << 14));
-}
-
 // Transposing LDS read (gfx950 ds_read_b64_tr_b16): within each 16-lane group, lane
 // i = 4a + b receives element b of the 4-element reads of lanes a, 4+a, 8+a, 12+a. When
 // lane s of a group points at k-row k0 + s/4, column m0 + 4 (s % 4) of a k-outer tile,
@@ -244,37 +172,6 @@ __device__ __forceinline__ void st_row16(uint16_t* p, u32x4 v) {
 #else
   *(u32x4*)p = v;
 #endif
-}
-
-// Workgroup barrier that the compiler may not move LDS or global accesses across (the
-// builtin alone is not a memory operation for it); emits only s_barrier.
-__device__ __forceinline__ void block_sync() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1, fully unrolled.
-template <int I, int N, class F>
-__device__ __forceinline__ void static_for_impl(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for_impl<I + 1, N>(f);
-  }
-}
-template <int N, class F>
-__device__ __forceinline__ void static_for(F&& f) { static_for_impl<0, N>(f); }
-
-// Calls f(std::integral_constant<int, n>) for a runtime n in [0, N].
-template <int N, class F>
-__device__ __forceinline__ void dispatch_count(int n, F&& f) {
-  if constexpr (N == 0) {
-    f(std::integral_constant<int, 0>{});
-  } else {
-    if (n >= N) f(std::integral_constant<int, N>{});
-    else dispatch_count<N - 1>(n, f);
-  }
 }
 
 template <class C, bool KRAG, int BKIND, int EPI>
@@ -315,53 +212,8 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
 
   // ---------------------------------------------------------------- tile list
   int total;
-  if constexpr (KRAG) {
-    total = p.G * p.m_tiles * p.n_tiles;
-  } else {
-    int loc[GPT];
-    int sum = 0;
-#pragma unroll
-    for (int i = 0; i < GPT; ++i) {
-      const int g = tid * GPT + i;
-      int c = 0;
-      if (g < p.G) {
-        const int mg = p.offsets[g + 1] - p.offsets[g];
-        c = ((mg + BM - 1) / BM) * p.n_tiles;
-      }
-      loc[i] = c;
-      sum += c;
-    }
-    s_scan[tid] = sum;
-    __syncthreads();
-    for (int off = 1; off < NT; off <<= 1) {
-      const int v = (tid >= off) ? s_scan[tid - off] : 0;
-      __syncthreads();
-      s_scan[tid] += v;
-      __syncthreads();
-    }
-    int run = s_scan[tid] - sum;
-#pragma unroll
-    for (int i = 0; i < GPT; ++i) {
-      const int g = tid * GPT + i;
-      if (g < p.G) s_pref[g] = run;
-      run += loc[i];
-    }
-    total = s_scan[NT - 1];
-    if (tid == 0) s_pref[p.G] = total;
-    __syncthreads();
-  }
-
-  // GROUP_M rasterization of a tile inside its expert: super-rows of group_m m-tiles, each
-  // swept over all n-tiles with the m index fastest.
-  auto raster = [&](int local, int mtiles, int &mt, int &nt) __attribute__((always_inline)) {
-    const int gm = p.group_m;
-    const int per_super = gm * p.n_tiles;
-    const int sr = local / per_super;
-    const int rem = local - sr * per_super;
-    const int rows = min(gm, mtiles - sr * gm);
-    nt = rem / rows;
-    mt = sr * gm + (rem - nt * rows);
-  };
+  if constexpr (KRAG) total = p.G * p.m_tiles * p.n_tiles;
+  else total = build_tile_prefix<NT, BM>(p.offsets, p.G, p.n_tiles, s_pref, s_scan);
 
   // Per-lane fragment offsets inside a stage (element units): offset = base[i] + step[s][h].
   int abase[FM], bbase[FN], astep[KS][2], bstep[KS][2];
@@ -402,23 +254,18 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
 #ifndef MOE_XCD_MAP
 #define MOE_XCD_MAP 1
 #endif
-  const int first = (MOE_XCD_MAP && (nblk & 7) == 0) ? ((b & 7) * (nblk >> 3) + (b >> 3)) : b;
+  const int first = MOE_XCD_MAP ? xcd_first_tile(b, nblk) : b;
 
   for (int tile = first; tile < total; tile += nblk) {
     int g, mt, nt;
     if constexpr (KRAG) {
       const int per = p.m_tiles * p.n_tiles;
       g = tile / per;
-      raster(tile - g * per, p.m_tiles, mt, nt);
+      raster_tile(tile - g * per, p.m_tiles, p.group_m, p.n_tiles, mt, nt);
     } else {
-      int lo = 0, hi = p.G;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_pref[mid] <= tile) lo = mid; else hi = mid;
-      }
-      g = lo;
+      g = tile_group(s_pref, p.G, tile);
       const int mg = p.offsets[g + 1] - p.offsets[g];
-      raster(tile - s_pref[g], (mg + BM - 1) / BM, mt, nt);
+      raster_tile(tile - s_pref[g], (mg + BM - 1) / BM, p.group_m, p.n_tiles, mt, nt);
     }
     g = __builtin_amdgcn_readfirstlane(g);
     mt = __builtin_amdgcn_readfirstlane(mt);
@@ -430,16 +277,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
     const int nk = (Kg + BK - 1) / BK;
     int m0 = mt * BM;
     int Me = Mg;                           // end (exclusive) of this tile's rows
-    if constexpr (!KRAG) {
-      // A group's 32-row fragments are dealt out evenly over its m-tiles (588 rows: 7, 6 and 6
-      // fragments, not 8, 8 and 3), so the m-tiles that share an expert's weight panel do
-      // nearly equal MFMA work and stay in step over the k-loop; a short last tile would run
-      // ahead and lose the panel's L2 lines before its siblings read them.
-      const int nm = (Mg + BM - 1) / BM;
-      const int F = (Mg + 31) / 32;
-      m0 = 32 * ((mt * F) / nm);
-      Me = min(32 * (((mt + 1) * F) / nm), Mg);
-    }
+    if constexpr (!KRAG) balanced_rows<BM>(mt, Mg, m0, Me);
     const int n0 = nt * BN;
     const int j0 = nt * (BN / 2);          // gate_up: first gate/linear column pair
     const uint16_t* Bg = p.B + (int64_t)g * p.b_gstride;
