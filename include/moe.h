@@ -249,6 +249,75 @@ moe_status moe_router_bwd(const float* gates, const float* dp, int64_t T, int k,
                           float* dlogits_kept, hipStream_t stream);
 
 /*
+ * W4A8 expert forward ("Frontier-scale RL with Kimi K3", section "Low precision (MXFP4)
+ * rollouts": the rollout engine runs the MoE layers with 4-bit weights and 8-bit
+ * activations; the explainer's "Idea Four": MXFP4 values in small blocks that share one
+ * scale). Forward only. The pages fix no formats; this library reads them as OCP
+ * Microscaling v1.0:
+ *   - MXFP4 row of n elements: n/2 code bytes, E2M1 element 2j in the low nibble of byte j
+ *     and 2j+1 in the high nibble (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 for codes 0..7,
+ *     sign in bit 3), plus n/32 scale bytes X + 127 (block of 32 scaled by 2^X,
+ *     X = floor(log2(amax)) - 2 clamped to [-127, 127], -127 for an all-zero block).
+ *     Elements round to nearest, ties to even, from v / 2^X and saturate to +-6.
+ *   - MXFP8 activations: the format of moe_mxfp8_quantize (E4M3, X = floor(log2 amax) - 8).
+ *   - Blocks run along the reduction dimension: x [T, d] and w_gu[e] [2H, d] along d;
+ *     a [R, H] and w_down[e] [d, H] along H.
+ * The products run on the block-scaled MFMA (fp32 accumulation; its per-block sums are not
+ * round-to-nearest fp32 sums: results agree with an exact sum to about 2^-13 of the sum of
+ * magnitudes at worst). d and H must be multiples of 128 (MOE_ERR_UNSUPPORTED otherwise).
+ */
+
+/*
+ * moe_mxfp4_quantize - v [rows, n] bf16 -> codes [rows, n/2] uint8, scales [rows, n/32]
+ * uint8 in the MXFP4 format above. moe_mxfp4_dequantize - the inverse, out [rows, n] bf16
+ * (exact: each value is an E2M1 value times a power of two). n must be a multiple of 32
+ * (MOE_ERR_UNSUPPORTED otherwise); v and out 16-byte aligned, codes 4-byte aligned.
+ */
+moe_status moe_mxfp4_quantize(const void* v, int64_t rows, int n, void* codes, void* scales,
+                              hipStream_t stream);
+moe_status moe_mxfp4_dequantize(const void* codes, const void* scales, int64_t rows, int n,
+                                void* out, hipStream_t stream);
+
+/*
+ * moe_grouped_gemm_gate_up_w4a8 - for every local expert e and its rows r, with x8 and w4
+ * the values of the MXFP8 x and the MXFP4 w_gu:
+ *   h[r, :]  = bf16( x8[row_token[r], :] . w4_gu[e]^T )       (not stored)
+ *   a[r, j]  = bf16( SiTU-GLU(h[r, j], h[r, H + j]) ), j < H
+ *   a_codes, a_scales = MXFP8 of a, blocks of 32 along H: the down GEMM's input.
+ * The dispatch (row gather through row_token) is fused into the operand load.
+ *   x_codes [T, d] uint8 and x_scales [T, d/32] uint8 (moe_mxfp8_quantize of x);
+ *   row_token [R_cap], expert_offsets [E_loc+1] (device) from moe_permute;
+ *   w_gu_codes [E_loc, 2H, d/2] and w_gu_scales [E_loc, 2H, d/32] (moe_mxfp4_quantize of
+ *   w_gu viewed as [E_loc * 2H, d]); a_codes [R_cap, H] out, a_scales [R_cap, H/32] out.
+ * Alignment: x_codes, w_gu_codes, a_codes 16 bytes; x_scales, w_gu_scales 4 bytes.
+ * Errors: as moe_grouped_gemm_gate_up, plus T < 0, T * d >= 2^32.
+ */
+moe_status moe_grouped_gemm_gate_up_w4a8(const void* x_codes, const void* x_scales, int64_t T,
+                                         const int32_t* row_token,
+                                         const int32_t* expert_offsets, int E_loc,
+                                         int64_t R_cap, int d, int H, const void* w_gu_codes,
+                                         const void* w_gu_scales, float beta, float linear_beta,
+                                         void* a_codes, void* a_scales, hipStream_t stream);
+
+/*
+ * moe_grouped_gemm_down_combine_w4a8 - moe_grouped_gemm_down_combine on W4A8 operands:
+ * o[r, :] = a8[r, :] . w4_down[e]^T, y[t, :] = bf16( sum_j p_j o[slot_row[t, j], :] ).
+ *   a_codes [R_cap, H], a_scales [R_cap, H/32] from moe_grouped_gemm_gate_up_w4a8;
+ *   w_down_codes [E_loc, d, H/2], w_down_scales [E_loc, d, H/32] (moe_mxfp4_quantize of
+ *   w_down viewed as [E_loc * d, H]); y [T, d] bf16 out; ws of
+ *   moe_workspace_size(MOE_WS_DOWN_COMBINE, ...) bytes (bf16(p o) rows).
+ * Alignment: a_codes, w_down_codes, y, ws 16 bytes; a_scales, w_down_scales 4 bytes.
+ * Errors: as moe_grouped_gemm_down_combine, plus R_cap * H >= 2^32.
+ */
+moe_status moe_grouped_gemm_down_combine_w4a8(const void* a_codes, const void* a_scales,
+                                              const int32_t* expert_offsets,
+                                              const float* row_gate, const int32_t* slot_row,
+                                              int64_t T, int k, int E_loc, int64_t R_cap, int H,
+                                              int d, const void* w_down_codes,
+                                              const void* w_down_scales, void* y, void* ws,
+                                              size_t ws_bytes, hipStream_t stream);
+
+/*
  * moe_workspace_size - bytes of `ws` the entry point `which` needs for these sizes
  * (arguments that do not apply are ignored). Host-only; launches nothing.
  */

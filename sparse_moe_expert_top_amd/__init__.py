@@ -7,14 +7,18 @@ from ._lib import (MoEError, load, workspace_size, header_functions, LIB_PATH,
                    moe_route_topk, moe_permute, moe_unpermute, moe_grouped_gemm_gate_up,
                    situ_glu_fwd, situ_glu_bwd, moe_grouped_gemm_down_combine, moe_expert_bwd,
                    moe_router_bwd, moe_grouped_gemm_gate_up_mx, moe_expert_bwd_mx,
-                   moe_mxfp8_quantize, moe_mxfp8_dequantize, MOE_WS_PERMUTE, MOE_WS_SITU_GLU_FWD, MOE_WS_SITU_GLU_BWD,
-                   MOE_WS_DOWN_COMBINE, MOE_WS_EXPERT_BWD)
-from .layer import LayerShape, LayerBuffers
+                   moe_mxfp8_quantize, moe_mxfp8_dequantize, moe_mxfp4_quantize,
+                   moe_mxfp4_dequantize, moe_grouped_gemm_gate_up_w4a8,
+                   moe_grouped_gemm_down_combine_w4a8, MOE_WS_PERMUTE, MOE_WS_SITU_GLU_FWD,
+                   MOE_WS_SITU_GLU_BWD, MOE_WS_DOWN_COMBINE, MOE_WS_EXPERT_BWD)
+from .layer import LayerShape, LayerBuffers, W4A8Weights
 
 __all__ = [
     "MoEError", "load", "workspace_size", "header_functions", "LIB_PATH", "moe_route_topk",
     "moe_permute", "moe_unpermute", "moe_grouped_gemm_gate_up", "situ_glu_fwd", "situ_glu_bwd",
     "moe_grouped_gemm_down_combine", "moe_expert_bwd", "moe_router_bwd",
     "moe_grouped_gemm_gate_up_mx", "moe_expert_bwd_mx", "moe_mxfp8_quantize",
-    "moe_mxfp8_dequantize", "LayerShape", "LayerBuffers",
+    "moe_mxfp8_dequantize", "moe_mxfp4_quantize", "moe_mxfp4_dequantize",
+    "moe_grouped_gemm_gate_up_w4a8", "moe_grouped_gemm_down_combine_w4a8", "LayerShape",
+    "LayerBuffers", "W4A8Weights",
 ]

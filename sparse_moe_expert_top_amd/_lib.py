@@ -60,6 +60,12 @@ _SIGS = {
                                _P, _F, _F, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_mxfp8_quantize": (_I, [_P, _I64, _I, _P, _P, _P]),
     "moe_mxfp8_dequantize": (_I, [_P, _P, _I64, _I, _P, _P]),
+    "moe_mxfp4_quantize": (_I, [_P, _I64, _I, _P, _P, _P]),
+    "moe_mxfp4_dequantize": (_I, [_P, _P, _I64, _I, _P, _P]),
+    "moe_grouped_gemm_gate_up_w4a8": (_I, [_P, _P, _I64, _P, _P, _I, _I64, _I, _I, _P, _P, _F,
+                                           _F, _P, _P, _P]),
+    "moe_grouped_gemm_down_combine_w4a8": (_I, [_P, _P, _P, _P, _P, _I64, _I, _I, _I64, _I, _I,
+                                                _P, _P, _P, _P, _SZ, _P]),
     "moe_workspace_size": (_I, [_I, _I64, _I, _I, _I, _I, _I64, ctypes.POINTER(_SZ)]),
 }
 
@@ -351,6 +357,87 @@ def moe_mxfp8_dequantize(codes, scales, out=None, stream=None):
     _check("moe_mxfp8_dequantize", load().moe_mxfp8_dequantize(_ptr(codes), _ptr(scales), rows,
                                                                n, _ptr(out), _stream(stream)))
     return out
+
+
+def moe_mxfp4_quantize(v, codes=None, scales=None, stream=None):
+    """bf16 [rows, n] -> (packed E2M1 codes uint8 [rows, n/2], scale bytes uint8 [rows, n/32])."""
+    rows, n = v.shape
+    _need(v, "v", torch.bfloat16)
+    codes = (torch.empty((rows, n // 2), dtype=torch.uint8, device=v.device)
+             if codes is None else codes)
+    scales = (torch.empty((rows, n // 32), dtype=torch.uint8, device=v.device)
+              if scales is None else scales)
+    _need(codes, "codes", torch.uint8, (rows, n // 2))
+    _need(scales, "scales", torch.uint8, (rows, n // 32))
+    _check("moe_mxfp4_quantize", load().moe_mxfp4_quantize(_ptr(v), rows, n, _ptr(codes),
+                                                           _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def moe_mxfp4_dequantize(codes, scales, out=None, stream=None):
+    """(packed codes [rows, n/2], scale bytes [rows, n/32]) -> bf16 [rows, n]."""
+    rows, half = codes.shape
+    n = 2 * half
+    _need(codes, "codes", torch.uint8)
+    _need(scales, "scales", torch.uint8, (rows, n // 32))
+    out = torch.empty((rows, n), dtype=torch.bfloat16, device=codes.device) if out is None else out
+    _need(out, "out", torch.bfloat16, (rows, n))
+    _check("moe_mxfp4_dequantize", load().moe_mxfp4_dequantize(_ptr(codes), _ptr(scales), rows,
+                                                               n, _ptr(out), _stream(stream)))
+    return out
+
+
+def moe_grouped_gemm_gate_up_w4a8(x_codes, x_scales, row_token, offsets, w_gu_codes,
+                                  w_gu_scales, R_cap, beta=4.0, linear_beta=25.0, a_codes=None,
+                                  a_scales=None, stream=None):
+    """W4A8 gate/up + SiTU-GLU: MXFP8 x [T, d] (+ scales), MXFP4 w_gu [E_loc, 2H, d/2]
+    (+ scales [E_loc, 2H, d/32]) -> a as MXFP8 (codes [R_cap, H], scales [R_cap, H/32])."""
+    T, d = x_codes.shape
+    E_loc, H2, _ = w_gu_codes.shape
+    H = H2 // 2
+    _need(x_codes, "x_codes", torch.uint8, (T, d))
+    _need(x_scales, "x_scales", torch.uint8, (T, d // 32))
+    _need(w_gu_codes, "w_gu_codes", torch.uint8, (E_loc, 2 * H, d // 2))
+    _need(w_gu_scales, "w_gu_scales", torch.uint8, (E_loc, 2 * H, d // 32))
+    _need(row_token, "row_token", torch.int32)
+    dev = x_codes.device
+    a_codes = (torch.empty((R_cap, H), dtype=torch.uint8, device=dev)
+               if a_codes is None else a_codes)
+    a_scales = (torch.empty((R_cap, H // 32), dtype=torch.uint8, device=dev)
+                if a_scales is None else a_scales)
+    _need(a_codes, "a_codes", torch.uint8, (R_cap, H))
+    _need(a_scales, "a_scales", torch.uint8, (R_cap, H // 32))
+    _check("moe_grouped_gemm_gate_up_w4a8", load().moe_grouped_gemm_gate_up_w4a8(
+        _ptr(x_codes), _ptr(x_scales), T, _ptr(row_token), _ptr(offsets), E_loc, R_cap, d, H,
+        _ptr(w_gu_codes), _ptr(w_gu_scales), beta, linear_beta, _ptr(a_codes), _ptr(a_scales),
+        _stream(stream)))
+    return a_codes, a_scales
+
+
+def moe_grouped_gemm_down_combine_w4a8(a_codes, a_scales, offsets, row_gate, slot_row,
+                                       w_down_codes, w_down_scales, R_cap, y=None, ws=None,
+                                       stream=None):
+    """W4A8 down GEMM + combine: MXFP8 a, MXFP4 w_down [E_loc, d, H/2] (+ scales
+    [E_loc, d, H/32]) -> y [T, d] bf16."""
+    E_loc, d, half = w_down_codes.shape
+    H = 2 * half
+    T, k = slot_row.shape
+    _need(a_codes, "a_codes", torch.uint8, (R_cap, H))
+    _need(a_scales, "a_scales", torch.uint8, (R_cap, H // 32))
+    _need(w_down_codes, "w_down_codes", torch.uint8)
+    _need(w_down_scales, "w_down_scales", torch.uint8, (E_loc, d, H // 32))
+    _need(row_gate, "row_gate", torch.float32)
+    _need(slot_row, "slot_row", torch.int32)
+    dev = a_codes.device
+    y = torch.empty((T, d), dtype=torch.bfloat16, device=dev) if y is None else y
+    _need(y, "y", torch.bfloat16, (T, d))
+    need = workspace_size(MOE_WS_DOWN_COMBINE, T=T, E_loc=E_loc, k=k, d=d, H=H, R_cap=R_cap)
+    ws = _ws(need, dev) if ws is None else ws
+    _check("moe_grouped_gemm_down_combine_w4a8", load().moe_grouped_gemm_down_combine_w4a8(
+        _ptr(a_codes), _ptr(a_scales), _ptr(offsets), _ptr(row_gate), _ptr(slot_row), T, k,
+        E_loc, R_cap, H, d, _ptr(w_down_codes), _ptr(w_down_scales), _ptr(y), _ptr(ws),
+        ws.numel(), _stream(stream)))
+    return y
 
 
 def moe_router_bwd(gates, dp, out=None, stream=None):

@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmoe.so")
 
-SOURCES = ["api.hip", "route_permute.hip", "situ.hip", "gemm.hip", "mxfp8.hip"]
+SOURCES = ["api.hip", "route_permute.hip", "situ.hip", "gemm.hip", "gemm_w4a8.hip",
+           "mxfp8.hip"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

@@ -42,6 +42,13 @@ static size_t bwd_dp_bytes(int64_t R_cap, int H) {
   return round256((size_t)gemm_da_slots(H) * (size_t)R_cap * 4);
 }
 
+static inline bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+// The W4A8 GEMMs advance K in stages of 128 (four 32-element scale blocks per row).
+static bool w4a8_dims_ok(int d, int H) {
+  return d > 0 && H > 0 && d % 128 == 0 && H % 128 == 0 && d <= (1 << 16) && H <= (1 << 16);
+}
+
 static bool layer_dims_ok(int d, int H) {
   return d > 0 && H > 0 && d % 64 == 0 && H % 64 == 0 && d <= (1 << 16) && H <= (1 << 16);
 }
@@ -333,6 +340,84 @@ moe_status moe_mxfp8_dequantize(const void* codes, const void* scales, int64_t r
   if (!aligned16(codes) || !aligned16(out)) return MOE_ERR_UNSUPPORTED;
   return hip_status(launch_mx_dequantize((const uint8_t*)codes, (const uint8_t*)scales, rows, n,
                                          (uint16_t*)out, stream));
+}
+
+moe_status moe_mxfp4_quantize(const void* v, int64_t rows, int n, void* codes, void* scales,
+                              hipStream_t stream) {
+  if (rows < 0 || n < 1) return MOE_ERR_SHAPE;
+  if (n % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!v || !codes || !scales) return MOE_ERR_NULL;
+  if (!aligned16(v) || !aligned4(codes)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_mx4_quantize((const uint16_t*)v, rows, n, (uint8_t*)codes,
+                                        (uint8_t*)scales, stream));
+}
+
+moe_status moe_mxfp4_dequantize(const void* codes, const void* scales, int64_t rows, int n,
+                                void* out, hipStream_t stream) {
+  if (rows < 0 || n < 1) return MOE_ERR_SHAPE;
+  if (n % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!codes || !scales || !out) return MOE_ERR_NULL;
+  if (!aligned4(codes) || !aligned16(out)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_mx4_dequantize((const uint8_t*)codes, (const uint8_t*)scales, rows, n,
+                                          (uint16_t*)out, stream));
+}
+
+moe_status moe_grouped_gemm_gate_up_w4a8(const void* x_codes, const void* x_scales, int64_t T,
+                                         const int32_t* row_token,
+                                         const int32_t* expert_offsets, int E_loc,
+                                         int64_t R_cap, int d, int H, const void* w_gu_codes,
+                                         const void* w_gu_scales, float beta, float linear_beta,
+                                         void* a_codes, void* a_scales, hipStream_t stream) {
+  if (T < 0 || E_loc < 1 || R_cap < 0) return MOE_ERR_SHAPE;
+  if (E_loc > 1024 || !w4a8_dims_ok(d, H) || R_cap >= (int64_t)1 << 31) return MOE_ERR_UNSUPPORTED;
+  if (T * (int64_t)d >= (int64_t)1 << 32) return MOE_ERR_UNSUPPORTED;
+  if (!(beta > 0.0f) || !(linear_beta > 0.0f)) return MOE_ERR_SHAPE;
+  if (!expert_offsets || !w_gu_codes || !w_gu_scales) return MOE_ERR_NULL;
+  if (R_cap == 0) return MOE_OK;
+  if (!x_codes || !x_scales || !row_token || !a_codes || !a_scales) return MOE_ERR_NULL;
+  if (!aligned16(x_codes) || !aligned4(x_scales) || !aligned16(w_gu_codes) ||
+      !aligned4(w_gu_scales) || !aligned16(a_codes))
+    return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_w4a8_gate_up(
+      (const uint8_t*)x_codes, (const uint8_t*)x_scales, row_token, expert_offsets, E_loc, R_cap,
+      d, H, (const uint8_t*)w_gu_codes, (const uint8_t*)w_gu_scales,
+      make_situ_coef(beta, linear_beta), (uint8_t*)a_codes, (uint8_t*)a_scales, stream));
+}
+
+moe_status moe_grouped_gemm_down_combine_w4a8(const void* a_codes, const void* a_scales,
+                                              const int32_t* expert_offsets,
+                                              const float* row_gate, const int32_t* slot_row,
+                                              int64_t T, int k, int E_loc, int64_t R_cap, int H,
+                                              int d, const void* w_down_codes,
+                                              const void* w_down_scales, void* y, void* ws,
+                                              size_t ws_bytes, hipStream_t stream) {
+  if (T < 0 || k < 1 || E_loc < 1 || R_cap < 0) return MOE_ERR_SHAPE;
+  if (k > 32 || E_loc > 1024 || !w4a8_dims_ok(d, H) || R_cap >= (int64_t)1 << 31)
+    return MOE_ERR_UNSUPPORTED;
+  if (T * (int64_t)k >= (int64_t)1 << 31 || !rows_addressable(T, d, H) ||
+      R_cap * (int64_t)H >= (int64_t)1 << 32)
+    return MOE_ERR_UNSUPPORTED;
+  if (!expert_offsets || !w_down_codes || !w_down_scales) return MOE_ERR_NULL;
+  if (T > 0 && (!slot_row || !y)) return MOE_ERR_NULL;
+  if (R_cap > 0 && (!a_codes || !a_scales || !row_gate || !ws)) return MOE_ERR_NULL;
+  if (ws_bytes < round256((size_t)R_cap * d * 2)) return MOE_ERR_WORKSPACE;
+  if ((a_codes && !aligned16(a_codes)) || (a_scales && !aligned4(a_scales)) ||
+      !aligned16(w_down_codes) || !aligned4(w_down_scales) || (y && !aligned16(y)) ||
+      (ws && !aligned16(ws)))
+    return MOE_ERR_UNSUPPORTED;
+  uint16_t* rows = (uint16_t*)ws;
+  if (R_cap > 0) {
+    hipError_t e = launch_w4a8_down((const uint8_t*)a_codes, (const uint8_t*)a_scales,
+                                    expert_offsets, row_gate, E_loc, R_cap, H, d,
+                                    (const uint8_t*)w_down_codes, (const uint8_t*)w_down_scales,
+                                    rows, stream);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if (T == 0) return MOE_OK;
+  // rows were already scaled by p in the GEMM epilogue, so the combine is a plain sum
+  return hip_status(launch_unpermute(rows, slot_row, nullptr, T, k, d, (uint16_t*)y, stream));
 }
 
 moe_status moe_router_bwd(const float* gates, const float* dp, int64_t T, int k,

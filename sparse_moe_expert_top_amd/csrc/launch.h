@@ -75,4 +75,23 @@ hipError_t launch_mx_quantize(const uint16_t* v, int64_t rows, int n, uint8_t* c
 hipError_t launch_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int n,
                                 uint16_t* out, hipStream_t s);
 
+// W4A8 forward ("Frontier-scale RL with Kimi K3", "Low precision (MXFP4) rollouts"): MXFP8
+// activations x MXFP4 weights on the block-scaled MFMA; K (d for gate_up, H for down) a
+// multiple of 128. gate_up writes a as MXFP8 (codes [R, H], scales [R, H/32]); down writes
+// bf16(p o) rows [R, d].
+hipError_t launch_w4a8_gate_up(const uint8_t* x_codes, const uint8_t* x_scales,
+                               const int32_t* row_token, const int32_t* offsets, int E_loc,
+                               int64_t R_cap, int d, int H, const uint8_t* w_codes,
+                               const uint8_t* w_scales, SituCoef c, uint8_t* a_codes,
+                               uint8_t* a_scales, hipStream_t s);
+hipError_t launch_w4a8_down(const uint8_t* a_codes, const uint8_t* a_scales,
+                            const int32_t* offsets, const float* row_gate, int E_loc,
+                            int64_t R_cap, int H, int d, const uint8_t* w_codes,
+                            const uint8_t* w_scales, uint16_t* rows_out, hipStream_t s);
+// MXFP4 format of the W4A8 weights (mxfp4.h); n a multiple of 32.
+hipError_t launch_mx4_quantize(const uint16_t* v, int64_t rows, int n, uint8_t* codes,
+                               uint8_t* scales, hipStream_t s);
+hipError_t launch_mx4_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int n,
+                                 uint16_t* out, hipStream_t s);
+
 }  // namespace moe

@@ -11,6 +11,12 @@ With h_store="mxfp8" the saved h is kept block-wise in FP8 instead ("Kimi K3 ...
 unified activation manager: most saved activations are block-wise FP8), through
 moe_grouped_gemm_gate_up_mx and moe_expert_bwd_mx.
 
+W4A8 forward ("Frontier-scale RL with Kimi K3", "Low precision (MXFP4) rollouts": rollouts
+run the MoE layers with 4-bit weights and 8-bit activations), forward only:
+    moe_route_topk -> moe_permute -> moe_mxfp8_quantize(x) -> moe_grouped_gemm_gate_up_w4a8
+    -> moe_grouped_gemm_down_combine_w4a8
+with the weights quantized once to MXFP4 (`W4A8Weights`).
+
 `LayerBuffers` allocates every buffer once (torch, HBM) so a training step issues only the
 library's kernels; buffers indexed by routed rows are sized by a capacity R_cap (T*k by
 default, which never overflows).
@@ -35,6 +41,22 @@ class LayerShape:
     H: int
     beta: float = 4.0
     linear_beta: float = 25.0
+
+
+class W4A8Weights:
+    """MXFP4 form of the expert weights for the W4A8 forward (quantized once, kept in HBM):
+    gu codes [E_loc, 2H, d/2] + scales [E_loc, 2H, d/32], down codes [E_loc, d, H/2] + scales
+    [E_loc, d, H/32], blocks along the reduction dimension."""
+
+    def __init__(self, w_gu, w_down):
+        E_loc, H2, d = w_gu.shape
+        H = H2 // 2
+        gq, gs = _lib.moe_mxfp4_quantize(w_gu.reshape(E_loc * H2, d))
+        dq, ds = _lib.moe_mxfp4_quantize(w_down.reshape(E_loc * d, H))
+        self.gu_codes = gq.view(E_loc, H2, d // 2)
+        self.gu_scales = gs.view(E_loc, H2, d // 32)
+        self.down_codes = dq.view(E_loc, d, H // 2)
+        self.down_scales = ds.view(E_loc, d, H // 32)
 
 
 class LayerBuffers:
@@ -97,6 +119,28 @@ class LayerBuffers:
         _lib.moe_grouped_gemm_down_combine(self.a, self.perm["offsets"], self.perm["row_gate"],
                                            self.perm["slot_row"], w_down, self.R_cap, y=self.y,
                                            ws=self.ws_down)
+        return self.y
+
+    def forward_w4a8(self, x, logits, w4: W4A8Weights):
+        """W4A8 forward: x quantized to MXFP8 per token, a to MXFP8 per row; y in bf16."""
+        s = self.shape
+        if getattr(self, "x_codes", None) is None:
+            dev = x.device
+            R = max(self.R_cap, 1)
+            self.x_codes = torch.empty((s.T, s.d), dtype=torch.uint8, device=dev)
+            self.x_scales = torch.empty((s.T, s.d // 32), dtype=torch.uint8, device=dev)
+            self.a_codes = torch.empty((R, s.H), dtype=torch.uint8, device=dev)
+            self.a_scales = torch.empty((R, s.H // 32), dtype=torch.uint8, device=dev)
+        self.route(logits)
+        _lib.moe_mxfp8_quantize(x, codes=self.x_codes, scales=self.x_scales)
+        _lib.moe_grouped_gemm_gate_up_w4a8(self.x_codes, self.x_scales, self.perm["row_token"],
+                                           self.perm["offsets"], w4.gu_codes, w4.gu_scales,
+                                           self.R_cap, s.beta, s.linear_beta,
+                                           a_codes=self.a_codes, a_scales=self.a_scales)
+        _lib.moe_grouped_gemm_down_combine_w4a8(self.a_codes, self.a_scales, self.perm["offsets"],
+                                                self.perm["row_gate"], self.perm["slot_row"],
+                                                w4.down_codes, w4.down_scales, self.R_cap,
+                                                y=self.y, ws=self.ws_down)
         return self.y
 
     def backward(self, dy, x, w_gu, w_down):

@@ -140,3 +140,53 @@ def test_mxfp8_entry_points_reject(lib):
     assert bw(*a) == EUNSUP
     a = list(base); a[9] = 0
     assert bw(*a) == ESHAPE
+
+
+def test_w4a8_entry_points_reject(lib):
+    """Host-side validation of the MXFP4 codec and the W4A8 GEMMs (nothing is launched)."""
+    P = ctypes.c_void_p(256)
+    U16 = ctypes.c_void_p(264)                                         # 8- but not 16-byte aligned
+    U4 = ctypes.c_void_p(258)                                          # not 4-byte aligned
+    assert lib.moe_mxfp4_quantize(P, 10, 48, P, P, None) == EUNSUP    # n % 32
+    assert lib.moe_mxfp4_quantize(P, -1, 64, P, P, None) == ESHAPE
+    assert lib.moe_mxfp4_quantize(P, 10, 64, P, None, None) == ENULL
+    assert lib.moe_mxfp4_quantize(U16, 10, 64, P, P, None) == EUNSUP  # v alignment
+    assert lib.moe_mxfp4_quantize(P, 10, 64, U4, P, None) == EUNSUP   # codes alignment
+    assert lib.moe_mxfp4_quantize(None, 0, 64, None, None, None) == OK
+    assert lib.moe_mxfp4_dequantize(P, P, 10, 40, P, None) == EUNSUP
+    assert lib.moe_mxfp4_dequantize(P, None, 10, 64, P, None) == ENULL
+    assert lib.moe_mxfp4_dequantize(P, P, 0, 64, None, None) == OK
+    gu = lib.moe_grouped_gemm_gate_up_w4a8
+    #        xc xs  T    tok off E_loc R_cap d   H   wc ws beta  lbeta ac as stream
+    ok = [P, P, 100, P, P, 4, 100, 256, 128, P, P, 4.0, 25.0, P, P, None]
+    def g(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return gu(*a)
+    assert g(a7=192) == EUNSUP                                         # d % 128
+    assert g(a8=64) == EUNSUP                                          # H % 128
+    assert g(a2=-1) == ESHAPE
+    assert g(a2=1 << 25) == EUNSUP                                     # T * d >= 2^32
+    assert g(a12=0.0) == ESHAPE                                        # linear_beta
+    assert g(a10=None) == ENULL                                        # weight scales
+    assert g(a14=None) == ENULL                                        # a scales
+    assert g(a0=U16) == EUNSUP                                         # x codes alignment
+    assert g(a1=U4) == EUNSUP                                          # x scales alignment
+    assert g(a13=U16) == EUNSUP                                        # a codes alignment
+    assert g(a6=0, a0=None, a1=None, a3=None, a13=None, a14=None) == OK   # R_cap = 0
+    dn = lib.moe_grouped_gemm_down_combine_w4a8
+    #          ac as off gate slot T   k  E_loc R_cap H    d   wc ws y  ws   bytes  stream
+    okd = [P, P, P, P, P, 100, 2, 4, 100, 128, 256, P, P, P, P, 1 << 30, None]
+    def dd(**kw):
+        a = list(okd)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return dn(*a)
+    assert dd(a9=192) == EUNSUP                                        # H % 128
+    assert dd(a15=10) == EWS
+    assert dd(a1=None) == ENULL
+    assert dd(a12=None) == ENULL
+    assert dd(a1=U4) == EUNSUP
+    assert dd(a8=1 << 24, a9=1024) == EUNSUP                           # R_cap * H >= 2^32
+    assert dd(a6=0) == ESHAPE

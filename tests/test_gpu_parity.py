@@ -502,3 +502,176 @@ def test_layer_mxfp8_store(moe, name):
     b16 = oracle.expert_layer_bwd(inp["x"], inp["dy"], inp["w_gu"], inp["w_down"], perm, cfg.H,
                                   mode="S")
     assert rel_err(b16["dp"], b["dp"]) > FP32_TOL
+
+
+# ------------------------------------------------------------------ W4A8 forward (MXFP4 weights)
+W4A8_CASES = {
+    "w4a8_tiny": LayerConfig("w4a8_tiny", T=256, d=256, H=128, E=8, k=2, e_lo=0, E_loc=8),
+    # several m- and n-tiles, ragged experts, five K stages, a partial gate/up tile pair
+    "w4a8_mid": LayerConfig("w4a8_mid", T=2048, d=640, H=384, E=16, k=4, e_lo=2, E_loc=10),
+    "w4a8_none_local": LayerConfig("w4a8_none_local", T=128, d=128, H=128, E=64, k=2, e_lo=60,
+                                   E_loc=4),
+}
+
+
+def e4m3_step(v, X):
+    """Spacing of the E4M3 grid (scaled by 2^X) at magnitude |v|."""
+    a = np.abs(v) / np.ldexp(1.0, X)
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))
+    return np.ldexp(1.0, (e - 3).astype(np.int64) + X)
+
+
+def check_a_codes(got_c, got_s, f, rows, H, beta, what):
+    """a as MXFP8 against the oracle's (f: oracle result, rows: its rows to compare).
+
+    The GPU takes h from the block-scaled MFMA, whose per-block sums deviate from exact ones
+    by up to about 2^-12.7 of the sum of the products' magnitudes (measured), then rounds h
+    and a to bf16 and encodes a; a code may therefore differ from the oracle's where a value
+    sits near a rounding boundary. Bound per element: one E4M3 step of either side, one bf16
+    step of a, and the h error carried through SiTU-GLU, |da| <= 1.2 |l| dg + min(beta, |g|) dl
+    with dh = 2^-11 sum|x8 w4| + one bf16 step of h. Nearly all codes must be identical."""
+    from oracle import mxfp8
+    ref_c, ref_s = f["a_codes"][rows], f["a_scales"][rows]
+    if ref_c.size == 0:
+        return
+    g = mxfp8.dequantize(got_c, got_s)
+    r = mxfp8.dequantize(ref_c, ref_s)
+    X = np.maximum(got_s, ref_s).astype(np.int64).repeat(32, axis=1) - 127
+    hg, hl = f["h"][rows][:, :H], f["h"][rows][:, H:]
+    mg, ml = f["h_mag"][rows][:, :H], f["h_mag"][rows][:, H:]
+    dg = 2.0 ** -11 * mg + 2.0 ** -7 * np.abs(hg)
+    dl = 2.0 ** -11 * ml + 2.0 ** -7 * np.abs(hl)
+    tol = (np.maximum(e4m3_step(r, X), e4m3_step(g, X)) + 2.0 ** -7 * np.abs(r)
+           + 1.2 * np.abs(hl) * dg + np.minimum(beta, np.abs(hg)) * dl)
+    diff = np.abs(g - r)
+    bad = diff > tol
+    same = float(np.mean(got_c == ref_c))
+    worst = np.unravel_index(np.argmax(diff / tol), diff.shape)
+    say(what, f"a codes identical {same:.5f}, scales identical {float(np.mean(got_s == ref_s)):.5f},"
+        f" worst |da|/tol {float(diff[worst] / tol[worst]):.3f} at {worst}: gpu {g[worst]:.6g}"
+        f" oracle {r[worst]:.6g} tol {tol[worst]:.3g} step {e4m3_step(r, X)[worst]:.3g}"
+        f" h {hg[worst]:.6g},{hl[worst]:.6g} sum|x w| {mg[worst]:.4g},{ml[worst]:.4g}")
+    assert not bad.any(), (what, np.argwhere(bad)[:5])
+    assert same >= 0.99, (what, same)
+
+
+def run_w4a8(m, cfg, inp, R_cap=None):
+    shape = m.LayerShape(T=inp["x"].shape[0], E=cfg.E, k=cfg.k, e_lo=cfg.e_lo, E_loc=cfg.E_loc,
+                         d=cfg.d, H=cfg.H, beta=cfg.beta, linear_beta=cfg.linear_beta)
+    buf = m.LayerBuffers(shape, R_cap=R_cap)
+    x, logits = dev_bf16(inp["x"]), dev(inp["logits"])
+    w4 = m.W4A8Weights(dev_bf16(inp["w_gu"]), dev_bf16(inp["w_down"]))
+    buf.forward_w4a8(x, logits, w4)
+    torch.cuda.synchronize()
+    return buf, w4
+
+
+def test_mxfp4_quantize_dequantize(moe):
+    """The weight quantizer is bit-exact with the oracle's MXFP4 (packed codes and scale
+    bytes) and the dequantizer returns the stored values exactly."""
+    from moe_inputs import f32_to_bf16_bits
+    rng = np.random.default_rng(12)
+    rows, n = 300, 256
+    v = rng.standard_normal((rows, n)).astype(np.float32)
+    v *= np.exp(rng.uniform(-30, 30, size=(rows, 1))).astype(np.float32)
+    v[0, :32] = 0.0
+    v[1, :32] = -0.0
+    v[2, 5] = 1e4                                        # one outlier: the rest of the block rounds to 0
+    v[3, ::5] *= 7.0                                     # values in the saturation band
+    v[4, :64] = rng.standard_normal(64).astype(np.float32) * 1e-38
+    tab = np.array([0, 0.25, 0.5, 0.75, 1, 1.25, 1.5, 1.75, 2, 2.5, 3, 3.5, 4, 5, 6, 6.5], np.float32)
+    v[5, :16], v[5, 16:32] = tab, -tab                   # every rounding midpoint, scale X = 0
+    vb = f32_to_bf16_bits(v)
+    codes, scales = moe.moe_mxfp4_quantize(dev_bf16(vb))
+    back = moe.moe_mxfp4_dequantize(codes, scales)
+    torch.cuda.synchronize()
+    ref_c, ref_s = oracle.mxfp4.quantize(oracle.bf16_widen(vb))
+    assert np.array_equal(scales.cpu().numpy(), ref_s)
+    assert np.array_equal(codes.cpu().numpy(), ref_c)
+    assert np.array_equal(host_bf16(back), oracle.mxfp4.dequantize(ref_c, ref_s))
+
+
+def compare_w4a8_full(m, cfg, inp, R_cap=None):
+    idx, gates, perm = oracle_route_perm(inp, cfg)
+    buf, w4 = run_w4a8(m, cfg, inp, R_cap)
+    check_route_perm(buf, idx, gates, perm)
+    ref_xc, ref_xs = oracle.mxfp8.quantize(oracle.bf16_widen(inp["x"]))
+    assert np.array_equal(buf.x_codes.cpu().numpy(), ref_xc)
+    assert np.array_equal(buf.x_scales.cpu().numpy(), ref_xs)
+    wq = [oracle.mxfp4.quantize(oracle.bf16_widen(inp[k_])) for k_ in ("w_gu", "w_down")]
+    assert np.array_equal(w4.gu_codes.cpu().numpy(), wq[0][0])
+    assert np.array_equal(w4.gu_scales.cpu().numpy(), wq[0][1])
+    assert np.array_equal(w4.down_codes.cpu().numpy(), wq[1][0])
+    assert np.array_equal(w4.down_scales.cpu().numpy(), wq[1][1])
+    f = oracle.w4a8.expert_layer_fwd_w4a8(inp["x"], inp["w_gu"], inp["w_down"], perm, cfg.H,
+                                           cfg.beta, cfg.linear_beta)
+    R = perm["R"]
+    check_a_codes(buf.a_codes[:R].cpu().numpy(), buf.a_scales[:R].cpu().numpy(), f,
+                  np.arange(R), cfg.H, cfg.beta, cfg.name)
+    err = rel_err(host_bf16(buf.y), f["y"])
+    say(cfg.name, "R", R, f"y {err:.2e}")
+    assert err <= BF16_TOL
+    return buf, perm
+
+
+@pytest.mark.parametrize("name", list(W4A8_CASES))
+def test_w4a8_forward(moe, name):
+    cfg = W4A8_CASES[name]
+    say(f"w4a8 full {name}")
+    inp = layer_inputs(cfg, seed=0)
+    if name == "w4a8_none_local":
+        inp["logits"][:, cfg.e_lo:cfg.e_lo + cfg.E_loc] -= 100.0
+    buf, perm = compare_w4a8_full(moe, cfg, inp)
+    if name == "w4a8_none_local":
+        assert perm["R"] == 0 and not bool(buf.y.any())
+
+
+def test_w4a8_exact_capacity(moe):
+    """R_cap equal to the routed rows (the tightest legal buffers)."""
+    cfg = W4A8_CASES["w4a8_mid"]
+    inp = layer_inputs(cfg, seed=3)
+    _, _, perm = oracle_route_perm(inp, cfg)
+    compare_w4a8_full(moe, cfg, inp, R_cap=perm["R"])
+
+
+def test_w4a8_full_size_sampled(moe):
+    """The W4A8 forward at the shard workload's full size, compared on tokens whose local
+    routes all go to two sampled experts (the oracle quantizes only those experts' weights),
+    plus properties of the whole output."""
+    cfg = LAYER_CONFIGS["shard"]
+    say("w4a8 sampled shard: generating inputs")
+    inp = layer_inputs(cfg, seed=0)
+    idx, gates, perm = oracle_route_perm(inp, cfg)
+    say(f"w4a8 sampled shard: GPU forward (R={perm['R']})")
+    buf, w4 = run_w4a8(moe, cfg, inp)
+    check_route_perm(buf, idx, gates, perm)
+    rng = np.random.default_rng(0)
+    off = perm["offsets"]
+    exps = set(int(e) for e in rng.choice(cfg.E_loc, 2, replace=False))
+    row_exp = np.repeat(np.arange(cfg.E_loc), np.diff(off))
+    tok_all = perm["row_token"][: perm["R"]]
+    ok = np.ones(cfg.T, bool)
+    ok[tok_all[~np.isin(row_exp, list(exps))]] = False       # a route outside the sampled experts
+    cand = np.intersect1d(np.nonzero(ok)[0], tok_all)
+    toks = np.concatenate([rng.choice(cand, min(40, len(cand)), replace=False),
+                           rng.choice(np.setdiff1d(np.arange(cfg.T), tok_all), 4, replace=False)])
+    sub, rows = sub_perm(perm, toks)
+    say(f"w4a8 sampled shard: oracle on {len(rows)} rows of experts {sorted(exps)}")
+    # the oracle reads w[e] only for experts with rows, which in `sub` are the sampled ones
+    w_gu = {e: inp["w_gu"][e] for e in exps}
+    w_down = {e: inp["w_down"][e] for e in exps}
+    f = oracle.w4a8.expert_layer_fwd_w4a8(inp["x"], w_gu, w_down, sub, cfg.H, cfg.beta,
+                                           cfg.linear_beta)
+    toks = np.unique(toks)
+    tt = torch.from_numpy(toks).cuda()
+    rr = torch.from_numpy(rows).cuda()
+    check_a_codes(buf.a_codes[rr].cpu().numpy(), buf.a_scales[rr].cpu().numpy(), f,
+                  np.arange(len(rows)), cfg.H, cfg.beta, "shard sampled")
+    err = rel_err(host_bf16(buf.y[tt]), f["y"][toks])
+    say("w4a8 shard sampled", len(toks), "tokens", f"y {err:.2e}")
+    assert err <= BF16_TOL
+    nonlocal_tok = torch.from_numpy(np.setdiff1d(np.arange(cfg.T), tok_all)).cuda()
+    assert not bool(buf.y[nonlocal_tok].any())
+    assert bool(torch.isfinite(buf.y.float()).all())
+    del buf, w4
+    torch.cuda.empty_cache()
