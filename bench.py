@@ -30,6 +30,7 @@ METRIC = "MoE expert fwd+bwd TFLOP/s (% bf16 MFMA peak); SiTU-GLU GB/s (% HBM)"
 # digest they record; for any other sources `traffic` is null.
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "gate_up_shard_counters.md")
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (the W4A8 MFMA takes an fp8 operand)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 
@@ -262,6 +263,49 @@ def main():
                       "saved_activation_GB": round((R * 2 * cfg.H * (1 + 1 / 32) + cfg.T * cfg.d * 2) / 1e9, 3),
                       "steps": n_mx}
     del bmx
+    torch.cuda.empty_cache()
+
+    # W4A8 forward (rollouts): MXFP4 weights quantized once, x quantized to MXFP8 each step
+    print("[bench] W4A8 forward", file=sys.stderr, flush=True)
+    w4 = moe.W4A8Weights(w_gu, w_down)
+    b4 = moe.LayerBuffers(shape)
+    for _ in range(args.warmup):
+        b4.forward_w4a8(x, logits, w4)
+    torch.cuda.synchronize()
+    assert b4.rows() == R
+    ev4 = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        b4.route(logits)
+        moe.moe_mxfp8_quantize(x, codes=b4.x_codes, scales=b4.x_scales)
+        ev4[i][0].record(stream)
+        moe.moe_grouped_gemm_gate_up_w4a8(b4.x_codes, b4.x_scales, b4.perm["row_token"],
+                                          b4.perm["offsets"], w4.gu_codes, w4.gu_scales,
+                                          b4.R_cap, cfg.beta, cfg.linear_beta,
+                                          a_codes=b4.a_codes, a_scales=b4.a_scales)
+        ev4[i][1].record(stream)
+        moe.moe_grouped_gemm_down_combine_w4a8(b4.a_codes, b4.a_scales, b4.perm["offsets"],
+                                               b4.perm["row_gate"], b4.perm["slot_row"],
+                                               w4.down_codes, w4.down_scales, b4.R_cap,
+                                               y=b4.y, ws=b4.ws_down)
+        ev4[i][2].record(stream)
+    torch.cuda.synchronize()
+    ms_w4 = (time.perf_counter() - t0) * 1e3 / args.steps
+    gu4_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev4]))
+    dn4_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev4]))
+    flop_fwd = 6.0 * R * cfg.d * cfg.H
+    out["w4a8_fwd"] = {
+        "ms_per_step": round(ms_w4, 4), "value": round(flop_fwd / (ms_w4 * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s (forward, 6 R d H)", "steps": args.steps,
+        "bf16_fwd_ms": round(phases["route_permute"] + phases["gate_up"] + phases["down_combine"], 4),
+        "gate_up_ms": round(gu4_ms, 4),
+        "gate_up_TFLOPs": round(flop_gu / (gu4_ms * 1e-3) / 1e12, 2),
+        "gate_up_frac_fp8_peak": round(flop_gu / (gu4_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+        "down_combine_ms": round(dn4_ms, 4),
+        "weights_GB": round(cfg.E_loc * 3 * cfg.H * cfg.d * (0.5 + 1 / 32) / 1e9, 3),
+        "bf16_weights_GB": round(cfg.E_loc * 3 * cfg.H * cfg.d * 2 / 1e9, 3),
+    }
+    del b4, w4
     torch.cuda.empty_cache()
 
     tr = committed_traffic(args.workload)
