@@ -32,6 +32,7 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "gate_up_shard_counters.md")
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (the W4A8 MFMA takes an fp8 operand)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+SHARD_ROWS = 16456             # routed local rows of the shard workload's seed-0 logits
 
 
 def parse():
@@ -47,7 +48,45 @@ def parse():
                     help="only run 3 plain 1 GiB device copies (counter calibration)")
     ap.add_argument("--print-digest", action="store_true",
                     help="print the digest of the kernel sources and exit")
+    ap.add_argument("--blas-reference", action="store_true",
+                    help="only time torch's bf16 GEMMs (hipBLASLt) on the layer's shapes, as context")
     return ap.parse_args()
+
+
+def blas_reference(cfg, R):
+    """torch's bf16 GEMMs (hipBLASLt) on dense and per-expert batched forms of the layer's
+    contractions with the shard workload's mean rows per expert; contiguous operands. Context
+    for the grouped kernels' TFLOP/s, not part of the path."""
+    import torch
+    dev = "cuda"
+    d, H, E = cfg.d, cfg.H, cfg.E_loc
+    Re = R // E
+    g = torch.Generator(device=dev).manual_seed(0)
+    rnd = lambda *sh: torch.randn(*sh, device=dev, dtype=torch.bfloat16, generator=g)
+    a, w = rnd(R, d), rnd(d, 2 * H)
+    ab, wb = rnd(E, Re, d), rnd(E, d, 2 * H)
+    ah, wd = rnd(E, Re, H), rnd(E, H, d)
+    dht, xb = rnd(E, 2 * H, Re), rnd(E, Re, d)
+    sq = rnd(8192, 8192), rnd(8192, 8192)
+    cases = [("dense gate/up-sized [R,d]x[d,2H]", lambda: a @ w, 4.0 * R * d * H),
+             ("batched gate/up [E,R/E,d]x[E,d,2H]", lambda: torch.bmm(ab, wb), 4.0 * E * Re * d * H),
+             ("batched down [E,R/E,H]x[E,H,d]", lambda: torch.bmm(ah, wd), 2.0 * E * Re * d * H),
+             ("batched dW_gu [E,2H,R/E]x[E,R/E,d], bf16 out", lambda: torch.bmm(dht, xb), 4.0 * E * Re * d * H),
+             ("dense 8192^3", lambda: sq[0] @ sq[1], 2.0 * 8192 ** 3)]
+    out = {}
+    for name, fn, flop in cases:
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 20
+        out[name] = {"ms": round(ms, 4), "TFLOP/s": round(flop / (ms * 1e-3) / 1e12, 1)}
+    print(json.dumps({"blas_reference": out, "rows_per_expert": Re}))
 
 
 def kernel_source_digest():
@@ -162,6 +201,9 @@ def main():
 
     torch.cuda.set_device(0)
     cfg = LAYER_CONFIGS[args.workload]
+    if args.blas_reference:
+        blas_reference(cfg, SHARD_ROWS)
+        return
     print(f"[bench] generating inputs for {cfg.name}", file=sys.stderr, flush=True)
     inp = layer_inputs(cfg, seed=0)
     x, dy = bf16_dev(inp["x"], torch), bf16_dev(inp["dy"], torch)
