@@ -634,20 +634,24 @@ def test_w4a8_exact_capacity(moe):
     compare_w4a8_full(moe, cfg, inp, R_cap=perm["R"])
 
 
-def test_w4a8_full_size_sampled(moe):
-    """The W4A8 forward at the shard workload's full size, compared on tokens whose local
-    routes all go to two sampled experts (the oracle quantizes only those experts' weights),
-    plus properties of the whole output."""
-    cfg = LAYER_CONFIGS["shard"]
-    say("w4a8 sampled shard: generating inputs")
+@pytest.mark.parametrize("name", ["shard", "skew_tail"])
+def test_w4a8_full_size_sampled(moe, name):
+    """The W4A8 forward at a full-size workload (one rank's shard; the skewed window with
+    empty experts), compared on tokens whose local routes all go to two sampled experts of at
+    most 2000 rows (the oracle quantizes only those experts' weights), plus properties of the
+    whole output."""
+    cfg = LAYER_CONFIGS[name]
+    say(f"w4a8 sampled {name}: generating inputs")
     inp = layer_inputs(cfg, seed=0)
     idx, gates, perm = oracle_route_perm(inp, cfg)
-    say(f"w4a8 sampled shard: GPU forward (R={perm['R']})")
+    say(f"w4a8 sampled {name}: GPU forward (R={perm['R']})")
     buf, w4 = run_w4a8(moe, cfg, inp)
     check_route_perm(buf, idx, gates, perm)
     rng = np.random.default_rng(0)
     off = perm["offsets"]
-    exps = set(int(e) for e in rng.choice(cfg.E_loc, 2, replace=False))
+    counts = np.diff(off)
+    small = np.nonzero((counts > 0) & (counts <= 2000))[0]
+    exps = set(int(e) for e in rng.choice(small, min(2, len(small)), replace=False))
     row_exp = np.repeat(np.arange(cfg.E_loc), np.diff(off))
     tok_all = perm["row_token"][: perm["R"]]
     ok = np.ones(cfg.T, bool)
@@ -656,7 +660,7 @@ def test_w4a8_full_size_sampled(moe):
     toks = np.concatenate([rng.choice(cand, min(40, len(cand)), replace=False),
                            rng.choice(np.setdiff1d(np.arange(cfg.T), tok_all), 4, replace=False)])
     sub, rows = sub_perm(perm, toks)
-    say(f"w4a8 sampled shard: oracle on {len(rows)} rows of experts {sorted(exps)}")
+    say(f"w4a8 sampled {name}: oracle on {len(rows)} rows of experts {sorted(exps)}")
     # the oracle reads w[e] only for experts with rows, which in `sub` are the sampled ones
     w_gu = {e: inp["w_gu"][e] for e in exps}
     w_down = {e: inp["w_down"][e] for e in exps}
@@ -666,9 +670,9 @@ def test_w4a8_full_size_sampled(moe):
     tt = torch.from_numpy(toks).cuda()
     rr = torch.from_numpy(rows).cuda()
     check_a_codes(buf.a_codes[rr].cpu().numpy(), buf.a_scales[rr].cpu().numpy(), f,
-                  np.arange(len(rows)), cfg.H, cfg.beta, "shard sampled")
+                  np.arange(len(rows)), cfg.H, cfg.beta, f"{name} sampled")
     err = rel_err(host_bf16(buf.y[tt]), f["y"][toks])
-    say("w4a8 shard sampled", len(toks), "tokens", f"y {err:.2e}")
+    say(f"w4a8 {name} sampled", len(toks), "tokens", f"y {err:.2e}")
     assert err <= BF16_TOL
     nonlocal_tok = torch.from_numpy(np.setdiff1d(np.arange(cfg.T), tok_all)).cuda()
     assert not bool(buf.y[nonlocal_tok].any())
