@@ -583,15 +583,27 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
     static_assert(WN == 64, "epilogue lane mapping assumes 64-column wavefront blocks");
     static_assert(NW * 32 * EPS * 4 <= NS * (BM + BN) * BK * 2, "epilogue staging fits the ring");
     float* st = reinterpret_cast<float*>(ring) + wave * 32 * EPS;
+    // down: each block's row scales are loaded before the block is staged, all at once: a
+    // load issued between two output stores would wait for the earlier store too
+    // (vector-memory operations complete in order), one round trip per 8-row step.
+    constexpr bool ROW_SCALE = (EPI == EPI_ROWS_SCALED);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       if (i >= nfv) break;
+      const int rblk = m0 + wm * WM + i * 32;            // tile-relative row of block row 0
+      float rsc[4];
+      if constexpr (ROW_SCALE) {
+#pragma unroll
+        for (int ps = 0; ps < 4; ++ps) {
+          const int row = rblk + ps * 8 + (lane >> 3);
+          rsc[ps] = (row < Me) ? p.row_scale[r0 + row] : 0.0f;
+        }
+      }
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v)
           st[((v >> 2) * 8 + (lane >> 5) * 4 + (v & 3)) * EPS + j * 32 + (lane & 31)] = acc[i][j][v];
-      const int rblk = m0 + wm * WM + i * 32;            // tile-relative row of block row 0
       if constexpr (IS_GU) {
         // lane: 8 gate columns (cc) of row (ps*16 + lane/4) and the matching 8 linear columns;
         // the 4 lanes of a row hold 32 consecutive (32-aligned) gate and linear columns each:
@@ -666,7 +678,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
             if (rblk + row < Me && col < p.N) {
               const int64_t r = r0 + rblk + row;
               float sc = 1.0f;
-              if constexpr (EPI == EPI_ROWS_SCALED) sc = p.row_scale[r];
+              if constexpr (EPI == EPI_ROWS_SCALED) sc = rsc[ps];
               u32x4 o;
 #pragma unroll
               for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(cv[2 * q] * sc, cv[2 * q + 1] * sc);

@@ -293,6 +293,17 @@ __global__ __launch_bounds__(512, 2) void w4a8_gemm_kernel(W4A8Args p) {
     for (int i = 0; i < FM; ++i) {
       if (i >= nfv) break;
       const int rblk = m0 + wm * WM + i * 32;
+      // down: the block's row scales are loaded before it is staged, all at once (a load
+      // issued between two output stores would also wait for the earlier store: vector-memory
+      // operations complete in order)
+      float rsc[4];
+      if constexpr (!GU) {
+#pragma unroll
+        for (int ps = 0; ps < 4; ++ps) {
+          const int row = rblk + ps * 8 + (lane >> 3);
+          rsc[ps] = (row < Me) ? p.row_scale[r0 + row] : 0.0f;
+        }
+      }
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const int f0 = GU ? hf : 2 * hf, f1 = GU ? 2 + hf : 2 * hf + 1;
@@ -346,7 +357,7 @@ __global__ __launch_bounds__(512, 2) void w4a8_gemm_kernel(W4A8Args p) {
             const f32x4 c1 = *(const f32x4*)&stg[row * EPS + cc * 8 + 4];
             if (rblk + row < Me && col < p.N) {
               const int64_t r = r0 + rblk + row;
-              const float sc = p.row_scale[r];
+              const float sc = rsc[ps];
               u32x4 o;
               o[0] = pack_bf16x2(c0[0] * sc, c0[1] * sc);
               o[1] = pack_bf16x2(c0[2] * sc, c0[3] * sc);
