@@ -511,6 +511,9 @@ W4A8_CASES = {
     "w4a8_mid": LayerConfig("w4a8_mid", T=2048, d=640, H=384, E=16, k=4, e_lo=2, E_loc=10),
     "w4a8_none_local": LayerConfig("w4a8_none_local", T=128, d=128, H=128, E=64, k=2, e_lo=60,
                                    E_loc=4),
+    "w4a8_one_token": LayerConfig("w4a8_one_token", T=1, d=128, H=128, E=8, k=3, e_lo=0,
+                                  E_loc=8),
+    "w4a8_k_eq_E": LayerConfig("w4a8_k_eq_E", T=64, d=128, H=256, E=6, k=6, e_lo=0, E_loc=6),
 }
 
 
