@@ -56,6 +56,7 @@ __device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
   return v;
 }
 
+// NV = ceil(E / 64) exactly (the launcher instantiates 1..16, E <= 1024).
 template <int NV>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
                                                          int64_t T, int E, int k,
@@ -69,12 +70,19 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   const int64_t nwave = ((int64_t)gridDim.x * blockDim.x) >> 6;
   for (int64_t t = wave; t < T; t += nwave) {
     const float* row = logits + t * (int64_t)E;
+    // all of the row's loads first, so they are in flight together (a guarded load would be
+    // one round trip per 64 logits). NV = ceil(E / 64): only the last group can pass E, and
+    // its lanes past E re-read column E-1 (in bounds).
+    float val[NV];
+#pragma unroll
+    for (int i = 0; i + 1 < NV; ++i) val[i] = row[lane + 64 * i];
+    val[NV - 1] = row[min(lane + 64 * (NV - 1), E - 1)];
     uint64_t key[NV];
     uint32_t lmax = 0;                                // value word of the lane's best key
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int e = lane + 64 * i;
-      key[i] = (e < E) ? route_key(row[e], e) : 0;     // 0 is below every real key
+      key[i] = (e < E) ? route_key(val[i], e) : 0;     // 0 is below every real key
       const uint32_t hv = (uint32_t)(key[i] >> 32);
       lmax = hv > lmax ? hv : lmax;
     }
@@ -135,6 +143,18 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   }
 }
 
+// Launches route_topk_kernel<nv> for the runtime nv in [NV, 16].
+template <int NV>
+static void route_launch_nv(int nv, dim3 grid, const float* logits, int64_t T, int E, int k,
+                            int32_t* idx, float* gates, hipStream_t s) {
+  if constexpr (NV <= 16) {
+    if (nv == NV)
+      hipLaunchKernelGGL(route_topk_kernel<NV>, grid, dim3(256), 0, s, logits, T, E, k, idx, gates);
+    else
+      route_launch_nv<NV + 1>(nv, grid, logits, T, E, k, idx, gates, s);
+  }
+}
+
 hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int32_t* idx,
                              float* gates, hipStream_t s) {
   if (T == 0) return hipSuccess;
@@ -143,14 +163,8 @@ hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int32
   int64_t blocks = (waves_needed + 3) / 4;
   const int64_t cap = (int64_t)device_cu_count() * 32;
   if (blocks > cap) blocks = cap;
-  dim3 grid((unsigned)blocks), block(256);
-  if (nv <= 1) hipLaunchKernelGGL(route_topk_kernel<1>, grid, block, 0, s, logits, T, E, k, idx, gates);
-  else if (nv <= 2) hipLaunchKernelGGL(route_topk_kernel<2>, grid, block, 0, s, logits, T, E, k, idx, gates);
-  else if (nv <= 4) hipLaunchKernelGGL(route_topk_kernel<4>, grid, block, 0, s, logits, T, E, k, idx, gates);
-  else if (nv <= 8) hipLaunchKernelGGL(route_topk_kernel<8>, grid, block, 0, s, logits, T, E, k, idx, gates);
-  else if (nv <= 12) hipLaunchKernelGGL(route_topk_kernel<12>, grid, block, 0, s, logits, T, E, k, idx, gates);
-  else if (nv <= 14) hipLaunchKernelGGL(route_topk_kernel<14>, grid, block, 0, s, logits, T, E, k, idx, gates);
-  else hipLaunchKernelGGL(route_topk_kernel<16>, grid, block, 0, s, logits, T, E, k, idx, gates);
+  // NV must equal ceil(E / 64): the kernel reads groups 0 .. NV-2 unguarded
+  route_launch_nv<1>(nv, dim3((unsigned)blocks), logits, T, E, k, idx, gates, s);
   return hipGetLastError();
 }
 
