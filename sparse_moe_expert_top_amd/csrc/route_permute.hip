@@ -177,6 +177,15 @@ hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int32
 //               same expert is a popcount over a per-expert token bitmask, so rows follow
 //               token order exactly.
 constexpr int kPermTok = 256;
+// A token's k expert indices (k <= KM), loaded together: entries past k re-read entry k-1
+// (in bounds), so no load is guarded and none waits for the previous one. The kernels are
+// instantiated for KM = 16 (k <= 16) and KM = 32.
+template <int KM>
+__device__ __forceinline__ void load_token_routes(const int32_t* __restrict__ row, int k,
+                                                  int (&ev)[KM]) {
+#pragma unroll
+  for (int j = 0; j < KM; ++j) ev[j] = row[min(j, k - 1)];
+}
 
 int permute_blocks(int64_t T) { return (int)((T + kPermTok - 1) / kPermTok); }
 
@@ -185,6 +194,7 @@ size_t permute_ws_bytes(int64_t T, int E_loc) {
   return ((n * sizeof(int32_t) + 255) / 256) * 256;
 }
 
+template <int KM>
 __global__ __launch_bounds__(256) void permute_count_kernel(const int32_t* __restrict__ idx,
                                                             int64_t T, int k, int e_lo,
                                                             int E_loc, int nblk,
@@ -194,9 +204,12 @@ __global__ __launch_bounds__(256) void permute_count_kernel(const int32_t* __res
   __syncthreads();
   const int64_t t = (int64_t)blockIdx.x * kPermTok + threadIdx.x;
   if (t < T) {
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[t * k + j] - e_lo;
-      if ((unsigned)e < (unsigned)E_loc) atomicAdd(&hist[e], 1);
+    int ev[KM];
+    load_token_routes(idx + t * k, k, ev);
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      const int e = ev[j] - e_lo;
+      if (j < k && (unsigned)e < (unsigned)E_loc) atomicAdd(&hist[e], 1);
     }
   }
   __syncthreads();
@@ -242,6 +255,7 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* cnt, int n,
   }
 }
 
+template <int KM>
 __global__ __launch_bounds__(256) void permute_scatter_kernel(
     const int32_t* __restrict__ idx, const float* __restrict__ gates, int64_t T, int k,
     int e_lo, int E_loc, int nblk, const int32_t* __restrict__ base, int64_t R_cap,
@@ -255,16 +269,25 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
   const bool valid = t < T;
   const int w = tid >> 5;
   const uint32_t bit = 1u << (tid & 31);
+  int ev[KM];
   if (valid) {
-    for (int j = 0; j < k; ++j) {
-      const int e = idx[t * k + j] - e_lo;
-      if ((unsigned)e < (unsigned)E_loc) atomicOr(&mask[e * 8 + w], bit);
+    load_token_routes(idx + t * k, k, ev);
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      const int e = ev[j] - e_lo;
+      if (j < k && (unsigned)e < (unsigned)E_loc) atomicOr(&mask[e * 8 + w], bit);
     }
   }
   __syncthreads();
   if (!valid) return;
-  for (int j = 0; j < k; ++j) {
-    const int e = idx[t * k + j] - e_lo;
+  float gv[KM];
+  const float* grow = gates + t * k;
+#pragma unroll
+  for (int j = 0; j < KM; ++j) gv[j] = grow[min(j, k - 1)];
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
+    if (j >= k) break;
+    const int e = ev[j] - e_lo;
     int32_t row = -1;
     if ((unsigned)e < (unsigned)E_loc) {
       int rank = __popc(mask[e * 8 + w] & (bit - 1u));
@@ -273,7 +296,7 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
       if (r < R_cap) {
         row = (int32_t)r;
         row_token[r] = (int32_t)t;
-        row_gate[r] = gates[t * k + j];
+        row_gate[r] = gv[j];
       }
     }
     slot_row[t * k + j] = row;
@@ -287,14 +310,22 @@ hipError_t launch_permute(const int32_t* idx, const float* gates, int64_t T, int
   const int nblk = permute_blocks(T);
   int32_t* cnt = (int32_t*)ws;
   if (nblk > 0) {
-    hipLaunchKernelGGL(permute_count_kernel, dim3(nblk), dim3(256), 0, s, idx, T, k, e_lo,
-                       E_loc, nblk, cnt);
+    if (k <= 16)
+      hipLaunchKernelGGL(permute_count_kernel<16>, dim3(nblk), dim3(256), 0, s, idx, T, k, e_lo,
+                         E_loc, nblk, cnt);
+    else
+      hipLaunchKernelGGL(permute_count_kernel<32>, dim3(nblk), dim3(256), 0, s, idx, T, k, e_lo,
+                         E_loc, nblk, cnt);
   }
   hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(1024), 0, s, cnt, E_loc * nblk, nblk,
                      E_loc, R_cap, offsets, status);
   if (nblk > 0) {
-    hipLaunchKernelGGL(permute_scatter_kernel, dim3(nblk), dim3(256), 0, s, idx, gates, T, k,
-                       e_lo, E_loc, nblk, cnt, R_cap, row_token, row_gate, slot_row);
+    if (k <= 16)
+      hipLaunchKernelGGL(permute_scatter_kernel<16>, dim3(nblk), dim3(256), 0, s, idx, gates, T,
+                         k, e_lo, E_loc, nblk, cnt, R_cap, row_token, row_gate, slot_row);
+    else
+      hipLaunchKernelGGL(permute_scatter_kernel<32>, dim3(nblk), dim3(256), 0, s, idx, gates, T,
+                         k, e_lo, E_loc, nblk, cnt, R_cap, row_token, row_gate, slot_row);
   }
   return hipGetLastError();
 }
@@ -358,8 +389,17 @@ __global__ __launch_bounds__(256) void dp_row_reduce_kernel(float* __restrict__ 
   const int64_t R = offsets[E_loc];
   for (int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x; r < R;
        r += (int64_t)gridDim.x * 256) {
+    // loads in batches of 8 (in flight together), added in slot order
     float s = 0.0f;
-    for (int q = 0; q < nslots; ++q) s += part[(int64_t)q * R_cap + r];
+    int q = 0;
+    for (; q + 8 <= nslots; q += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(q + u) * R_cap + r];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; q < nslots; ++q) s += part[(int64_t)q * R_cap + r];
     part[r] = s;
   }
 }
