@@ -286,7 +286,7 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
   for (int j = 0; j < KM; ++j) gv[j] = grow[min(j, k - 1)];
 #pragma unroll
   for (int j = 0; j < KM; ++j) {
-    if (j >= k) break;
+    if (j >= k) continue;   // k is uniform; continue (not break) lets the loop unroll fully
     const int e = ev[j] - e_lo;
     int32_t row = -1;
     if ((unsigned)e < (unsigned)E_loc) {
