@@ -38,6 +38,8 @@ struct SituCoef {
   float beta;
   float lam;
   float bl;      // beta * lambda
+  float lam4;    // 4 lambda
+  float beta4;   // 4 beta
   int b4;        // beta == 4: exp(-|g|) = exp(-|g|/2)^2
 };
 
@@ -52,6 +54,8 @@ inline SituCoef make_situ_coef(float beta, float lam) {
   c.beta = beta;
   c.lam = lam;
   c.bl = beta * lam;
+  c.lam4 = 4.0f * lam;
+  c.beta4 = 4.0f * beta;
   c.b4 = (beta == 4.0f) ? 1 : 0;
   return c;
 }
@@ -88,29 +92,35 @@ __device__ __forceinline__ float situ_fwd(float g, float l, const SituCoef& c) {
   return __uint_as_float(__float_as_uint(mag) ^ sgn);
 }
 
-// Backward: dL/dg, dL/dl for upstream da.
+// Backward: dL/dg, dL/dl for upstream da. With p1 = 1 + e1, p2 = 1 + e2, p3 = 1 + e3,
+// u1 = 1 - e1, u3 = 1 - e3 and sn = (g >= 0 ? 1 : e2):
+//   tanh(g/beta) = sgn(g) u1 / p1,  sigmoid(g) = sn / p2,  tanh(l/lambda) = sgn(l) u3 / p3,
+//   1 - tanh^2(g/beta) = 4 e1 / p1^2,  s (1 - s) = e2 / p2^2,  1 - tanh^2(l/lambda) = 4 e3 / p3^2,
+// so over the common denominator (p1 p2 p3)^2, with s1 = sgn(g) u1,
+//   d gate'/dg = (4 e1 sn p2 + beta s1 e2 p1) / (p1 p2)^2,
+//   dL/dg = da lin' d gate'/dg = da lambda sgn(l) u3 (4 e1 sn p2 + beta s1 e2 p1) p3 / (p1 p2 p3)^2,
+//   dL/dl = da gate' 4 e3 / p3^2 = da 4 beta s1 sn e3 p1 p2 / (p1 p2 p3)^2,
+// one reciprocal in all (every p lies in [1, 2], so nothing overflows). With beta = 4 the
+// factor 4 of d gate'/dg moves into the constant 4 lambda. u1, u3, sn, the p's and the
+// reciprocal are the forward's own expressions, so a caller that needs both shares them.
 template <bool B4>
 __device__ __forceinline__ void situ_grad(float g, float l, float da, const SituCoef& c,
                                           float& dg, float& dl) {
   const float ag = fabsf(g), al = fabsf(l);
   float e1, e2, e3;
   situ_exps<B4>(ag, al, c, e1, e2, e3);
+  const float u1 = one_minus_exp(ag * c.y1, e1);
+  const float u3 = one_minus_exp(al * c.y3, e3);
+  const float sn = (g >= 0.0f) ? 1.0f : e2;
   const float p1 = 1.0f + e1, p2 = 1.0f + e2, p3 = 1.0f + e3;
   const float p12 = p1 * p2;
-  const float rall = rcp_fast(p12 * p3);             // 1 / (p1 p2 p3)
-  const float r12 = rall * p3;                       // 1 / (p1 p2)
-  const float r1 = r12 * p2, r2 = r12 * p1, r3 = rall * p12;
-  const float t1 = copysignf(one_minus_exp(ag * c.y1, e1) * r1, g);
-  const float s = ((g >= 0.0f) ? 1.0f : e2) * r2;
-  const float t2 = copysignf(one_minus_exp(al * c.y3, e3) * r3, l);
-  const float gate = (c.beta * t1) * s;
-  const float lin = c.lam * t2;
-  const float sech2_g = (4.0f * e1) * (r1 * r1);       // 1 - tanh^2(g/beta)
-  const float s1ms = e2 * (r2 * r2);                    // s (1 - s)
-  const float sech2_l = (4.0f * e3) * (r3 * r3);       // 1 - tanh^2(l/lambda)
-  const float dgate = sech2_g * s + (c.beta * t1) * s1ms;
-  dg = (da * lin) * dgate;
-  dl = (da * gate) * sech2_l;
+  const float rd = rcp_fast(p12 * p3);
+  const float rd2 = rd * rd;                         // 1 / (p1 p2 p3)^2
+  const float s1 = copysignf(u1, g);
+  const float ng = B4 ? (e1 * sn) * p2 + (s1 * e2) * p1                    // d gate'/dg / 4
+                      : ((4.0f * e1) * sn) * p2 + ((c.beta * s1) * e2) * p1;
+  dg = ((copysignf((B4 ? c.lam4 : c.lam) * u3, l) * da) * ng) * (rd2 * p3);
+  dl = (((s1 * sn) * (c.beta4 * e3)) * da) * (rd2 * p12);
 }
 
 // Backward with the recomputed activation: a is bit-identical to situ_fwd<B4>(g, l, c).
