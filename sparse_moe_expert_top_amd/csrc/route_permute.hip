@@ -333,28 +333,54 @@ hipError_t launch_permute(const int32_t* idx, const float* gates, int64_t T, int
 // ------------------------------------------------------------------------------ combine
 // out[t] = bf16( sum_j w(r) rows[r] ), r = slot_row[t, j] >= 0, in fp32 and slot order.
 // One workgroup per token at a time, sized to the row (one lane per 8 consecutive columns,
-// 16 bytes, up to 1024 lanes); the output row is written with streaming stores.
+// 16 bytes, up to 1024 lanes); the output row is written with streaming stores. Each wave
+// loads the token's k slot entries (and their weights) at once, one per lane, and walks only
+// the local ones, four at a time with all four row loads in flight before any add.
 __global__ __launch_bounds__(1024) void unpermute_kernel(const uint16_t* __restrict__ rows,
                                                         const int32_t* __restrict__ slot_row,
                                                         const float* __restrict__ w,
                                                         int64_t T, int k, int n,
                                                         uint16_t* __restrict__ out) {
   const int nc = n >> 3;
+  const int lane = threadIdx.x & 63;
   for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
-    const int32_t* sr = slot_row + t * k;
+    const int rl = (lane < k) ? slot_row[t * k + lane] : -1;
+    const float wl = (rl >= 0 && w) ? w[rl] : 1.0f;
+    const uint64_t live = __ballot(rl >= 0);
     for (int c = threadIdx.x; c < nc; c += blockDim.x) {
       float acc[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-      for (int j = 0; j < k; ++j) {
-        const int r = sr[j];
-        if (r < 0) continue;
-        const float wt = w ? w[r] : 1.0f;
-        const u32x4 v = *(const u32x4*)(rows + (int64_t)r * n + 8 * c);
+      uint64_t m = live;
+      while (m) {
+        int rb[4];
+        float wb[4];
+        int nb = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] += wt * bf16_lo(v[q]);
-          acc[2 * q + 1] += wt * bf16_hi(v[q]);
+        for (int b = 0; b < 4; ++b) {
+          rb[b] = 0;
+          wb[b] = 0.0f;
+          if (m) {
+            const int j = __builtin_ctzll(m);
+            m &= m - 1;
+            rb[b] = __builtin_amdgcn_readlane(rl, j);
+            wb[b] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), j));
+            nb = b + 1;
+          }
+        }
+        u32x4 v[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          if (b < nb) v[b] = *(const u32x4*)(rows + (int64_t)rb[b] * n + 8 * c);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          if (b < nb) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              acc[2 * q] += wb[b] * bf16_lo(v[b][q]);
+              acc[2 * q + 1] += wb[b] * bf16_hi(v[b][q]);
+            }
+          }
         }
       }
       u32x4 o;
