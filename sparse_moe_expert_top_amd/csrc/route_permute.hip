@@ -56,9 +56,12 @@ __device__ __forceinline__ uint64_t wave_max64(uint64_t v) {
   return v;
 }
 
-// NV = ceil(E / 64) exactly (the launcher instantiates 1..16, E <= 1024).
+// NV = ceil(E / 64) exactly (the launcher instantiates 1..16, E <= 1024). Each wavefront
+// spends most of a token waiting on dependent steps, so the kernel is compiled for five
+// wavefronts per SIMD (at most 96 VGPRs, no spills) rather than the four its free register
+// allocation gives.
 template <int NV>
-__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
+__global__ __launch_bounds__(256, 5) void route_topk_kernel(const float* __restrict__ logits,
                                                          int64_t T, int E, int k,
                                                          int32_t* __restrict__ idx_out,
                                                          float* __restrict__ gates_out) {
@@ -77,15 +80,19 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 #pragma unroll
     for (int i = 0; i + 1 < NV; ++i) val[i] = row[lane + 64 * i];
     val[NV - 1] = row[min(lane + 64 * (NV - 1), E - 1)];
-    uint64_t key[NV];
+    // value words of the keys (the index word of logit i is ~(lane + 64 i)); 0 for lanes
+    // past E, below every real key
+    uint32_t kv[NV];
     uint32_t lmax = 0;                                // value word of the lane's best key
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int e = lane + 64 * i;
-      key[i] = (e < E) ? route_key(val[i], e) : 0;     // 0 is below every real key
-      const uint32_t hv = (uint32_t)(key[i] >> 32);
-      lmax = hv > lmax ? hv : lmax;
+      kv[i] = (e < E) ? (uint32_t)(route_key(val[i], e) >> 32) : 0u;
+      lmax = kv[i] > lmax ? kv[i] : lmax;
     }
+    auto key = [&](int i) __attribute__((always_inline)) -> uint64_t {
+      return kv[i] ? (((uint64_t)kv[i] << 32) | (uint32_t)~(lane + 64 * i)) : 0;
+    };
     // largest thr with at least k lane maxima >= thr
     uint32_t thr = 0;
 #pragma unroll
@@ -93,10 +100,9 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
       const uint32_t c = thr | (1u << bit);
       if (__builtin_popcountll(__ballot(lmax >= c)) >= k) thr = c;
     }
-    const uint64_t thr_key = (uint64_t)thr << 32;
     int c = 0;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) c += (key[i] >= thr_key) ? 1 : 0;
+    for (int i = 0; i < NV; ++i) c += (kv[i] >= thr && kv[i] != 0) ? 1 : 0;
     int incl = c;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -109,11 +115,20 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
       int pos = incl - c;
 #pragma unroll
       for (int i = 0; i < NV; ++i)
-        if (key[i] >= thr_key) cand[wv][pos++] = key[i];
+        if (kv[i] >= thr && kv[i] != 0) cand[wv][pos++] = key(i);
       __builtin_amdgcn_wave_barrier();
       const uint64_t my = (lane < total) ? cand[wv][lane] : 0;
+      // rank among the candidates: broadcast reads, eight in flight at a time
       int rank = 0;
-      for (int j = 0; j < total; ++j) rank += (cand[wv][j] > my) ? 1 : 0;   // broadcast reads
+      int j = 0;
+      for (; j + 8 <= total; j += 8) {
+        uint64_t cj[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) cj[u] = cand[wv][j + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) rank += (cj[u] > my) ? 1 : 0;
+      }
+      for (; j < total; ++j) rank += (cand[wv][j] > my) ? 1 : 0;
       if (lane < total && rank < k) sel[wv][rank] = my;
       __builtin_amdgcn_wave_barrier();
       if (lane < k) mine = sel[wv][lane];
@@ -122,11 +137,11 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
       for (int j = 0; j < k; ++j) {
         uint64_t best = 0;
 #pragma unroll
-        for (int i = 0; i < NV; ++i) best = key[i] > best ? key[i] : best;
+        for (int i = 0; i < NV; ++i) best = key(i) > best ? key(i) : best;
         best = wave_max64(best);
 #pragma unroll
         for (int i = 0; i < NV; ++i)
-          if (key[i] == best) key[i] = 0;              // keys are unique: only the winner
+          if (key(i) == best) kv[i] = 0;               // keys are unique: only the winner
         if (lane == j) mine = best;
       }
     }

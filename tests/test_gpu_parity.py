@@ -215,11 +215,16 @@ def test_permute_capacity_overflow(moe):
     assert np.array_equal(out["row_token"][:R_cap].cpu().numpy(), perm["row_token"][:R_cap])
 
 
-def test_unpermute(moe):
-    rng = np.random.default_rng(2)
+@pytest.mark.parametrize("T,k,n", [(50, 5, 64), (40, 32, 3584), (3, 1, 8), (17, 9, 136)])
+def test_unpermute(moe, T, k, n):
+    """Combine: k = 32 (every lane of the slot load), several batches of four local slots
+    per token, rows narrower than a wave and a row of 3584 columns."""
+    say(f"unpermute T={T} k={k} n={n}")
+    rng = np.random.default_rng(2 + k)
     from moe_inputs import f32_to_bf16_bits
-    rows = f32_to_bf16_bits(rng.standard_normal((300, 64)).astype(np.float32))
-    slot_row = rng.integers(-1, 300, size=(50, 5)).astype(np.int32)
+    rows = f32_to_bf16_bits(rng.standard_normal((300, n)).astype(np.float32))
+    slot_row = rng.integers(-1, 300, size=(T, k)).astype(np.int32)
+    slot_row[0] = -1                       # a token with no local slot
     w = rng.random(300).astype(np.float32)
     out = moe.moe_unpermute(dev_bf16(rows), dev(slot_row), dev(w))
     out_nw = moe.moe_unpermute(dev_bf16(rows), dev(slot_row))
