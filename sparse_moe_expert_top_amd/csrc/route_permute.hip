@@ -80,18 +80,21 @@ __global__ __launch_bounds__(256, 5) void route_topk_kernel(const float* __restr
 #pragma unroll
     for (int i = 0; i + 1 < NV; ++i) val[i] = row[lane + 64 * i];
     val[NV - 1] = row[min(lane + 64 * (NV - 1), E - 1)];
-    // value words of the keys (the index word of logit i is ~(lane + 64 i)); 0 for lanes
-    // past E, below every real key
+    // value words of the keys (the index word of logit i is ~(lane + 64 i)); bit i of
+    // `live` marks logit i as present (lane + 64 i < E) and, in the many-ties path, not yet
+    // picked. An absent key reads as 0, below every real key.
     uint32_t kv[NV];
+    uint32_t live = 0;
     uint32_t lmax = 0;                                // value word of the lane's best key
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int e = lane + 64 * i;
       kv[i] = (e < E) ? (uint32_t)(route_key(val[i], e) >> 32) : 0u;
+      if (e < E) live |= 1u << i;
       lmax = kv[i] > lmax ? kv[i] : lmax;
     }
     auto key = [&](int i) __attribute__((always_inline)) -> uint64_t {
-      return kv[i] ? (((uint64_t)kv[i] << 32) | (uint32_t)~(lane + 64 * i)) : 0;
+      return ((live >> i) & 1u) ? (((uint64_t)kv[i] << 32) | (uint32_t)~(lane + 64 * i)) : 0;
     };
     // largest thr with at least k lane maxima >= thr
     uint32_t thr = 0;
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(256, 5) void route_topk_kernel(const float* __restr
     }
     int c = 0;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) c += (kv[i] >= thr && kv[i] != 0) ? 1 : 0;
+    for (int i = 0; i < NV; ++i) c += (((live >> i) & 1u) && kv[i] >= thr) ? 1 : 0;
     int incl = c;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -115,7 +118,7 @@ __global__ __launch_bounds__(256, 5) void route_topk_kernel(const float* __restr
       int pos = incl - c;
 #pragma unroll
       for (int i = 0; i < NV; ++i)
-        if (kv[i] >= thr && kv[i] != 0) cand[wv][pos++] = key(i);
+        if (((live >> i) & 1u) && kv[i] >= thr) cand[wv][pos++] = key(i);
       __builtin_amdgcn_wave_barrier();
       const uint64_t my = (lane < total) ? cand[wv][lane] : 0;
       // rank among the candidates: broadcast reads, eight in flight at a time
@@ -141,7 +144,7 @@ __global__ __launch_bounds__(256, 5) void route_topk_kernel(const float* __restr
         best = wave_max64(best);
 #pragma unroll
         for (int i = 0; i < NV; ++i)
-          if (key(i) == best) kv[i] = 0;               // keys are unique: only the winner
+          if (key(i) == best) live &= ~(1u << i);      // keys are unique: only the winner
         if (lane == j) mine = best;
       }
     }
