@@ -350,32 +350,38 @@ hipError_t launch_permute(const int32_t* idx, const float* gates, int64_t T, int
 
 // ------------------------------------------------------------------------------ combine
 // out[t] = bf16( sum_j w(r) rows[r] ), r = slot_row[t, j] >= 0, in fp32 and slot order.
-// One workgroup per token at a time, sized to the row (one lane per 8 consecutive columns,
-// 16 bytes, up to 1024 lanes); the output row is written with streaming stores. Each wave
-// loads the token's k slot entries (and their weights) at once, one per lane, and walks only
-// the local ones, four at a time with all four row loads in flight before any add.
-__global__ __launch_bounds__(1024) void unpermute_kernel(const uint16_t* __restrict__ rows,
+// One wavefront per token at a time, so a CU keeps as many tokens in flight as it holds
+// wavefronts. The wave loads the token's k slot entries (and their weights) at once, one per
+// lane, and walks only the local ones, two at a time; each lane owns CPL 16-byte column
+// chunks per pass, so the loads of a pass (2 x CPL per lane) are in flight together. The
+// output row is written with streaming stores.
+constexpr int kCombCPL = 4;
+__global__ __launch_bounds__(256) void unpermute_kernel(const uint16_t* __restrict__ rows,
                                                         const int32_t* __restrict__ slot_row,
                                                         const float* __restrict__ w,
                                                         int64_t T, int k, int n,
                                                         uint16_t* __restrict__ out) {
   const int nc = n >> 3;
   const int lane = threadIdx.x & 63;
-  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+  const int64_t nwave = (int64_t)gridDim.x * (blockDim.x >> 6);
+  for (int64_t t = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); t < T;
+       t += nwave) {
     const int rl = (lane < k) ? slot_row[t * k + lane] : -1;
     const float wl = (rl >= 0 && w) ? w[rl] : 1.0f;
     const uint64_t live = __ballot(rl >= 0);
-    for (int c = threadIdx.x; c < nc; c += blockDim.x) {
-      float acc[8];
+    for (int c0 = 0; c0 < nc; c0 += 64 * kCombCPL) {
+      float acc[kCombCPL][8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+      for (int u = 0; u < kCombCPL; ++u)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[u][q] = 0.0f;
       uint64_t m = live;
       while (m) {
-        int rb[4];
-        float wb[4];
+        int rb[2];
+        float wb[2];
         int nb = 0;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int b = 0; b < 2; ++b) {
           rb[b] = 0;
           wb[b] = 0.0f;
           if (m) {
@@ -386,25 +392,38 @@ __global__ __launch_bounds__(1024) void unpermute_kernel(const uint16_t* __restr
             nb = b + 1;
           }
         }
-        u32x4 v[4];
+        u32x4 v[2][kCombCPL];
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-          if (b < nb) v[b] = *(const u32x4*)(rows + (int64_t)rb[b] * n + 8 * c);
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          if (b < nb) {
+          for (int u = 0; u < kCombCPL; ++u) {
+            const int c = c0 + 64 * u + lane;
+            if (b < nb && c < nc) v[b][u] = *(const u32x4*)(rows + (int64_t)rb[b] * n + 8 * c);
+          }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              acc[2 * q] += wb[b] * bf16_lo(v[b][q]);
-              acc[2 * q + 1] += wb[b] * bf16_hi(v[b][q]);
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int u = 0; u < kCombCPL; ++u) {
+            const int c = c0 + 64 * u + lane;
+            if (b < nb && c < nc) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                acc[u][2 * q] += wb[b] * bf16_lo(v[b][u][q]);
+                acc[u][2 * q + 1] += wb[b] * bf16_hi(v[b][u][q]);
+              }
             }
           }
+      }
+#pragma unroll
+      for (int u = 0; u < kCombCPL; ++u) {
+        const int c = c0 + 64 * u + lane;
+        if (c < nc) {
+          u32x4 o;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[u][2 * q], acc[u][2 * q + 1]);
+          __builtin_nontemporal_store(o, (u32x4*)(out + t * n + 8 * c));
         }
       }
-      u32x4 o;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
-      __builtin_nontemporal_store(o, (u32x4*)(out + t * n + 8 * c));
     }
   }
 }
@@ -412,12 +431,10 @@ __global__ __launch_bounds__(1024) void unpermute_kernel(const uint16_t* __restr
 hipError_t launch_unpermute(const uint16_t* rows, const int32_t* slot_row, const float* w,
                             int64_t T, int k, int n, uint16_t* out, hipStream_t s) {
   if (T == 0 || n == 0) return hipSuccess;
-  const int nc = n / 8;
-  const int threads = nc >= 1024 ? 1024 : ((nc + 63) / 64) * 64;
-  int64_t blocks = T;
-  const int64_t cap = (int64_t)device_cu_count() * (16 * 256 / threads + 1);
+  int64_t blocks = (T + 3) / 4;
+  const int64_t cap = (int64_t)device_cu_count() * 16;
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL(unpermute_kernel, dim3((unsigned)blocks), dim3(threads), 0, s, rows,
+  hipLaunchKernelGGL(unpermute_kernel, dim3((unsigned)blocks), dim3(256), 0, s, rows,
                      slot_row, w, T, k, n, out);
   return hipGetLastError();
 }
