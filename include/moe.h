@@ -307,7 +307,7 @@ moe_status moe_grouped_gemm_gate_up_w4a8(const void* x_codes, const void* x_scal
  *   w_down viewed as [E_loc * d, H]); y [T, d] bf16 out; ws of
  *   moe_workspace_size(MOE_WS_DOWN_COMBINE, ...) bytes (bf16(p o) rows).
  * Alignment: a_codes, w_down_codes, y, ws 16 bytes; a_scales, w_down_scales 4 bytes.
- * Errors: as moe_grouped_gemm_down_combine, plus R_cap * H >= 2^32.
+ * Errors: as moe_grouped_gemm_down_combine.
  */
 moe_status moe_grouped_gemm_down_combine_w4a8(const void* a_codes, const void* a_scales,
                                               const int32_t* expert_offsets,

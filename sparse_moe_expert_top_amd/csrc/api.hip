@@ -396,8 +396,7 @@ moe_status moe_grouped_gemm_down_combine_w4a8(const void* a_codes, const void* a
   if (T < 0 || k < 1 || E_loc < 1 || R_cap < 0) return MOE_ERR_SHAPE;
   if (k > 32 || E_loc > 1024 || !w4a8_dims_ok(d, H) || R_cap >= (int64_t)1 << 31)
     return MOE_ERR_UNSUPPORTED;
-  if (T * (int64_t)k >= (int64_t)1 << 31 || !rows_addressable(T, d, H) ||
-      R_cap * (int64_t)H >= (int64_t)1 << 32)
+  if (T * (int64_t)k >= (int64_t)1 << 31 || !rows_addressable(T, d, H))
     return MOE_ERR_UNSUPPORTED;
   if (!expert_offsets || !w_down_codes || !w_down_scales) return MOE_ERR_NULL;
   if (T > 0 && (!slot_row || !y)) return MOE_ERR_NULL;

@@ -140,10 +140,16 @@ __global__ __launch_bounds__(512, 2) void w4a8_gemm_kernel(W4A8Args p) {
         return min(n0 + row, p.N - 1);
       }
     };
+    // A row of tile row `row`: gathered rows are token rows, addressed from A itself (the
+    // host keeps T * K below 2^32); contiguous rows are addressed from the tile's first row,
+    // so their 32-bit offsets stay below 256 K whatever the row count
     auto a_srow = [&](int row) __attribute__((always_inline)) {
       const int m = min(m0 + row, Me - 1);
-      return p.a_gather ? p.a_gather[r0 + m] : r0 + m;
+      return p.a_gather ? p.a_gather[r0 + m] : m - m0;
     };
+    const int64_t a_row0 = p.a_gather ? 0 : (int64_t)r0 + m0;
+    const uint8_t* a_tile = p.A + a_row0 * p.K;
+    const uint8_t* as_tile = p.As + a_row0 * ks;
 
     // ------------------------------------------------------------ load addressing
     uint32_t a_off[LA], b_off[LB], s_off;
@@ -163,13 +169,13 @@ __global__ __launch_bounds__(512, 2) void w4a8_gemm_kernel(W4A8Args p) {
     }
     // waves 0..3 load the A scales of rows 64 w .. 64 w + 63, waves 4..7 the B scales
     const bool s_is_a = wave_u < 4;
-    const uint8_t* s_src = s_is_a ? p.As : Bsg;
+    const uint8_t* s_src = s_is_a ? as_tile : Bsg;
     s_off = (uint32_t)(s_is_a ? a_srow(wave * 64 + lane) : w_row((wave - 4) * 64 + lane)) *
             (uint32_t)ks;
 
     auto issue = [&](int kt) __attribute__((always_inline)) {
       const uint32_t base = ring_lds + (kt % NS) * STAGE;
-      dma_saddr<LA>(base + wave_u * (LA * 1024), uniform_ptr(p.A + kt * BK), a_off);
+      dma_saddr<LA>(base + wave_u * (LA * 1024), uniform_ptr(a_tile + kt * BK), a_off);
       dma_saddr<LB>(base + A_BYTES + wave_u * (LB * 1024), uniform_ptr(Bg + kt * (BK / 2)), b_off);
       dma_saddr_b32(base + SC_OFF + wave_u * 256, uniform_ptr(s_src + kt * 4), s_off);
     };

@@ -188,5 +188,5 @@ def test_w4a8_entry_points_reject(lib):
     assert dd(a1=None) == ENULL
     assert dd(a12=None) == ENULL
     assert dd(a1=U4) == EUNSUP
-    assert dd(a8=1 << 24, a9=1024) == EUNSUP                           # R_cap * H >= 2^32
+    assert dd(a8=1 << 24, a9=1024) == EWS      # R_cap * H >= 2^32 is supported; ws too small
     assert dd(a6=0) == ESHAPE

@@ -642,6 +642,37 @@ def test_w4a8_exact_capacity(moe):
     compare_w4a8_full(moe, cfg, inp, R_cap=perm["R"])
 
 
+def test_w4a8_rows_past_4gib(moe):
+    """W4A8 with activation codes past 4 GiB: 140000 tokens routed to all 8 experts of H =
+    4096 give R * H = 4.6e9 bytes of a codes, so the down GEMM's rows of the last expert lie
+    beyond 2^32 bytes from the array's start. Tokens late in the batch (whose last-expert rows
+    are there) are compared with the oracle over all 8 experts."""
+    cfg = LayerConfig("w4a8_past_4gib", T=140000, d=256, H=4096, E=8, k=8, e_lo=0, E_loc=8)
+    say("w4a8 rows past 4 GiB: generating inputs")
+    inp = layer_inputs(cfg, seed=3)
+    idx, gates, perm = oracle_route_perm(inp, cfg)
+    assert perm["R"] * cfg.H > (1 << 32)
+    say(f"w4a8 rows past 4 GiB: GPU forward (R={perm['R']})")
+    buf, w4 = run_w4a8(moe, cfg, inp)
+    check_route_perm(buf, idx, gates, perm)
+    rng = np.random.default_rng(3)
+    toks = np.sort(rng.choice(np.arange(cfg.T - 20000, cfg.T), 12, replace=False))
+    sub, rows = sub_perm(perm, toks)
+    assert rows.max() * cfg.H >= (1 << 32)
+    say(f"w4a8 rows past 4 GiB: oracle on {len(rows)} rows")
+    f = oracle.w4a8.expert_layer_fwd_w4a8(inp["x"], inp["w_gu"], inp["w_down"], sub, cfg.H,
+                                           cfg.beta, cfg.linear_beta)
+    tt = torch.from_numpy(toks).cuda()
+    rr = torch.from_numpy(rows).cuda()
+    check_a_codes(buf.a_codes[rr].cpu().numpy(), buf.a_scales[rr].cpu().numpy(), f,
+                  np.arange(len(rows)), cfg.H, cfg.beta, "past 4 GiB")
+    err = rel_err(host_bf16(buf.y[tt]), f["y"][toks])
+    say("w4a8 rows past 4 GiB", len(toks), "tokens", f"y {err:.2e}")
+    assert err <= BF16_TOL
+    del buf, w4
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("name", ["shard", "skew_tail"])
 def test_w4a8_full_size_sampled(moe, name):
     """The W4A8 forward at a full-size workload (one rank's shard; the skewed window with
