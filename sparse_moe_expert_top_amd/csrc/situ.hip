@@ -7,12 +7,13 @@
 //
 // Here each lane owns 16-byte chunks (8 columns) of a row: it reads g and l (and da) with
 // 16-byte non-temporal loads, keeps all fp32 intermediates in registers and writes the
-// bf16 result with 16-byte non-temporal stores. The grid walks row-chunks in a grid-stride
-// loop, so the fp32 working set is fixed by the launch, not by R. Measured on MI355X at
-// R = 131072, H = 3072: a grid of 256 workgroups per CU (far more than are resident, so
-// the dispatcher keeps every CU's queue full as waves retire) with 2 chunks per lane per
-// step streams at 5.3-5.6 TB/s, against 4.6-4.9 TB/s for a persistent grid of 8 per CU
-// and the same for 1-8 chunks per step; plain (temporal) loads cost 5-10%.
+// bf16 result with 16-byte non-temporal stores. One launch covers every chunk once: a thread
+// takes KU chunks 256 apart and finds each chunk's row and column with one 32-bit division
+// by the chunks per row, so nothing is set up per thread beyond that. Launches are split by
+// rows so each covers fewer than 2^32 chunks. No memory beyond the inputs and outputs is
+// used, whatever R. Measured on MI355X at R = 131072, H = 3072: 5.5-5.7 TB/s forward
+// (KU = 4) and 6.0 TB/s backward (KU = 2), against 5.4-5.6 TB/s for a grid-stride walk of
+// 256 workgroups per CU; plain (temporal) loads cost 5-10 %.
 #include <hip/hip_runtime.h>
 
 #include "common.h"
@@ -21,23 +22,12 @@
 
 namespace moe {
 
-// Grid-stride walk over (row, 16-byte chunk) pairs without a division per step: the
-// stride is added as (dr rows, dc chunks) with a carry. Each thread advances kU strides per
-// iteration and issues all kU chunks' loads before any arithmetic, keeping kU x 32 (fwd)
-// or kU x 48 (bwd) bytes in flight per lane.
-#ifndef MOE_SITU_UNROLL
-#define MOE_SITU_UNROLL 2
-#endif
-#ifndef MOE_SITU_BLOCKS_PER_CU
-#define MOE_SITU_BLOCKS_PER_CU 256
-#endif
 #ifndef MOE_SITU_NT_LOAD
 #define MOE_SITU_NT_LOAD 1
 #endif
 #ifndef MOE_SITU_NT_STORE
 #define MOE_SITU_NT_STORE 1
 #endif
-constexpr int kU = MOE_SITU_UNROLL;
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
 #if MOE_SITU_NT_LOAD
@@ -54,126 +44,124 @@ __device__ __forceinline__ void st16(u32x4 v, uint16_t* p) {
 #endif
 }
 
-struct ChunkWalk {
-  int64_t r, dr;
-  int cc, dc, hc;
-  __device__ void init(int64_t i0, int64_t stride, int hc_) {
-    hc = hc_;
-    dr = stride / hc;
-    dc = (int)(stride - dr * hc);
-    r = i0 / hc;
-    cc = (int)(i0 - r * hc);
-  }
-  __device__ void step() {
-    r += dr;
-    cc += dc;
-    if (cc >= hc) { cc -= hc; r += 1; }
-  }
-};
+// Chunks per thread: the forward's four loads and the backward's six per chunk pair keep
+// enough bytes in flight at these counts (measured best of 2 and 4 for each).
+constexpr int kFwdKU = 4;
+constexpr int kBwdKU = 2;
 
 template <bool B4>
 __global__ __launch_bounds__(256) void situ_fwd_kernel(const uint16_t* __restrict__ h,
-                                                       int64_t R, int H, SituCoef c,
-                                                       uint16_t* __restrict__ a) {
-  ChunkWalk w;
-  w.init((int64_t)blockIdx.x * blockDim.x + threadIdx.x, (int64_t)gridDim.x * blockDim.x,
-         H >> 3);
-  while (w.r < R) {
-    int64_t ro[kU];
-    int co[kU];
-    u32x4 g[kU], l[kU];
+                                                       uint32_t n, uint32_t hc, int H,
+                                                       SituCoef c, uint16_t* __restrict__ a) {
+  constexpr int KU = kFwdKU;
+  const uint32_t i0 = blockIdx.x * (256u * KU) + threadIdx.x;
+  u32x4 g[KU], l[KU];
+  uint32_t rr[KU], cc[KU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      ro[u] = w.r;
-      co[u] = w.cc;
-      if (w.r < R) {
-        const uint16_t* hr = h + w.r * (2 * (int64_t)H) + 8 * w.cc;
-        g[u] = ld16(hr);
-        l[u] = ld16(hr + H);
-      }
-      w.step();
+  for (int u = 0; u < KU; ++u) {
+    const uint32_t i = i0 + 256u * u;
+    rr[u] = i / hc;
+    cc[u] = i - rr[u] * hc;
+    if (i < n) {
+      const uint16_t* hr = h + (int64_t)rr[u] * (2 * H) + 8 * cc[u];
+      g[u] = ld16(hr);
+      l[u] = ld16(hr + H);
     }
+  }
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      if (ro[u] >= R) break;
-      u32x4 o;
+  for (int u = 0; u < KU; ++u) {
+    if (i0 + 256u * u >= n) break;
+    u32x4 o;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float a0 = situ_fwd<B4>(bf16_lo(g[u][q]), bf16_lo(l[u][q]), c);
-        const float a1 = situ_fwd<B4>(bf16_hi(g[u][q]), bf16_hi(l[u][q]), c);
-        o[q] = pack_bf16x2(a0, a1);
-      }
-      st16(o, a + ro[u] * (int64_t)H + 8 * co[u]);
+    for (int q = 0; q < 4; ++q) {
+      const float a0 = situ_fwd<B4>(bf16_lo(g[u][q]), bf16_lo(l[u][q]), c);
+      const float a1 = situ_fwd<B4>(bf16_hi(g[u][q]), bf16_hi(l[u][q]), c);
+      o[q] = pack_bf16x2(a0, a1);
     }
+    st16(o, a + (int64_t)rr[u] * H + 8 * cc[u]);
   }
 }
 
 template <bool B4>
 __global__ __launch_bounds__(256) void situ_bwd_kernel(const uint16_t* __restrict__ h,
                                                        const uint16_t* __restrict__ da,
-                                                       int64_t R, int H, SituCoef c,
-                                                       uint16_t* __restrict__ dh) {
-  ChunkWalk w;
-  w.init((int64_t)blockIdx.x * blockDim.x + threadIdx.x, (int64_t)gridDim.x * blockDim.x,
-         H >> 3);
-  while (w.r < R) {
-    int64_t ro[kU];
-    int co[kU];
-    u32x4 g[kU], l[kU], d[kU];
+                                                       uint32_t n, uint32_t hc, int H,
+                                                       SituCoef c, uint16_t* __restrict__ dh) {
+  constexpr int KU = kBwdKU;
+  const uint32_t i0 = blockIdx.x * (256u * KU) + threadIdx.x;
+  u32x4 g[KU], l[KU], d[KU];
+  uint32_t rr[KU], cc[KU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      ro[u] = w.r;
-      co[u] = w.cc;
-      if (w.r < R) {
-        const int64_t hoff = w.r * (2 * (int64_t)H) + 8 * w.cc;
-        g[u] = ld16(h + hoff);
-        l[u] = ld16(h + hoff + H);
-        d[u] = ld16(da + w.r * (int64_t)H + 8 * w.cc);
-      }
-      w.step();
+  for (int u = 0; u < KU; ++u) {
+    const uint32_t i = i0 + 256u * u;
+    rr[u] = i / hc;
+    cc[u] = i - rr[u] * hc;
+    if (i < n) {
+      const int64_t hoff = (int64_t)rr[u] * (2 * H) + 8 * cc[u];
+      g[u] = ld16(h + hoff);
+      l[u] = ld16(h + hoff + H);
+      d[u] = ld16(da + (int64_t)rr[u] * H + 8 * cc[u]);
     }
+  }
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      if (ro[u] >= R) break;
-      u32x4 og, ol;
+  for (int u = 0; u < KU; ++u) {
+    if (i0 + 256u * u >= n) break;
+    u32x4 og, ol;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float g0, l0, g1, l1;
-        situ_grad<B4>(bf16_lo(g[u][q]), bf16_lo(l[u][q]), bf16_lo(d[u][q]), c, g0, l0);
-        situ_grad<B4>(bf16_hi(g[u][q]), bf16_hi(l[u][q]), bf16_hi(d[u][q]), c, g1, l1);
-        og[q] = pack_bf16x2(g0, g1);
-        ol[q] = pack_bf16x2(l0, l1);
-      }
-      const int64_t hoff = ro[u] * (2 * (int64_t)H) + 8 * co[u];
-      st16(og, dh + hoff);
-      st16(ol, dh + hoff + H);
+    for (int q = 0; q < 4; ++q) {
+      float g0, l0, g1, l1;
+      situ_grad<B4>(bf16_lo(g[u][q]), bf16_lo(l[u][q]), bf16_lo(d[u][q]), c, g0, l0);
+      situ_grad<B4>(bf16_hi(g[u][q]), bf16_hi(l[u][q]), bf16_hi(d[u][q]), c, g1, l1);
+      og[q] = pack_bf16x2(g0, g1);
+      ol[q] = pack_bf16x2(l0, l1);
     }
+    const int64_t hoff = (int64_t)rr[u] * (2 * H) + 8 * cc[u];
+    st16(og, dh + hoff);
+    st16(ol, dh + hoff + H);
   }
 }
 
-static unsigned situ_grid(int64_t n) {
-  int64_t blocks = (n + 256 * kU - 1) / (256 * kU);
-  const int64_t cap = (int64_t)device_cu_count() * MOE_SITU_BLOCKS_PER_CU;
-  if (blocks > cap) blocks = cap;
-  return (unsigned)(blocks > 0 ? blocks : 1);
+// Rows per launch: each launch covers fewer than 2^32 chunks (H / 8 per row), with room for
+// the last block's overhang.
+static int64_t situ_rows_per_launch(int H) {
+  return (((int64_t)1 << 32) - 4096) / (H / 8);
 }
 
 hipError_t launch_situ_fwd(const uint16_t* h, int64_t R, int H, SituCoef c, uint16_t* a,
                            hipStream_t s) {
-  const int64_t n = R * (int64_t)(H / 8);
-  if (n == 0) return hipSuccess;
-  if (c.b4) hipLaunchKernelGGL(situ_fwd_kernel<true>, dim3(situ_grid(n)), dim3(256), 0, s, h, R, H, c, a);
-  else hipLaunchKernelGGL(situ_fwd_kernel<false>, dim3(situ_grid(n)), dim3(256), 0, s, h, R, H, c, a);
-  return hipGetLastError();
+  const uint32_t hc = (uint32_t)(H / 8);
+  const int64_t step = situ_rows_per_launch(H);
+  for (int64_t r0 = 0; r0 < R; r0 += step) {
+    const int64_t rows = (R - r0 < step) ? R - r0 : step;
+    const uint32_t n = (uint32_t)(rows * hc);
+    const unsigned blocks = (unsigned)((n + 256u * kFwdKU - 1) / (256u * kFwdKU));
+    const uint16_t* hp = h + r0 * 2 * H;
+    uint16_t* ap = a + r0 * H;
+    if (c.b4) hipLaunchKernelGGL(situ_fwd_kernel<true>, dim3(blocks), dim3(256), 0, s, hp, n, hc, H, c, ap);
+    else hipLaunchKernelGGL(situ_fwd_kernel<false>, dim3(blocks), dim3(256), 0, s, hp, n, hc, H, c, ap);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_situ_bwd(const uint16_t* h, const uint16_t* da, int64_t R, int H,
                            SituCoef c, uint16_t* dh, hipStream_t s) {
-  const int64_t n = R * (int64_t)(H / 8);
-  if (n == 0) return hipSuccess;
-  if (c.b4) hipLaunchKernelGGL(situ_bwd_kernel<true>, dim3(situ_grid(n)), dim3(256), 0, s, h, da, R, H, c, dh);
-  else hipLaunchKernelGGL(situ_bwd_kernel<false>, dim3(situ_grid(n)), dim3(256), 0, s, h, da, R, H, c, dh);
-  return hipGetLastError();
+  const uint32_t hc = (uint32_t)(H / 8);
+  const int64_t step = situ_rows_per_launch(H);
+  for (int64_t r0 = 0; r0 < R; r0 += step) {
+    const int64_t rows = (R - r0 < step) ? R - r0 : step;
+    const uint32_t n = (uint32_t)(rows * hc);
+    const unsigned blocks = (unsigned)((n + 256u * kBwdKU - 1) / (256u * kBwdKU));
+    const uint16_t* hp = h + r0 * 2 * H;
+    const uint16_t* dap = da + r0 * H;
+    uint16_t* dhp = dh + r0 * 2 * H;
+    if (c.b4) hipLaunchKernelGGL(situ_bwd_kernel<true>, dim3(blocks), dim3(256), 0, s, hp, dap, n, hc, H, c, dhp);
+    else hipLaunchKernelGGL(situ_bwd_kernel<false>, dim3(blocks), dim3(256), 0, s, hp, dap, n, hc, H, c, dhp);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace moe
