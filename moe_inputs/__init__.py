@@ -20,7 +20,6 @@ std is fan_in ** -0.5 (d for W_gate and W_up, H for W_down).
 """
 from __future__ import annotations
 
-import math
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -165,21 +164,3 @@ def situ_inputs(R: int, H: int, seed: int = 0, h_std: float = 3.0) -> dict:
     h = f32_to_bf16_bits(_normal(rng, (R, 2 * H), h_std))
     da = f32_to_bf16_bits(_normal(rng, (R, H), 1.0))
     return dict(h=h, da=da)
-
-
-def layer_flops(R: int, d: int, H: int) -> dict:
-    """Useful GEMM FLOPs of the layer (2 M N K per contraction, M = routed rows exactly)."""
-    f_gu = 2.0 * R * (2 * H) * d
-    f_dn = 2.0 * R * d * H
-    return dict(gate_up=f_gu, down=f_dn, dA=f_dn, dW_down=f_dn, dX=f_gu, dW_gu=f_gu,
-                fwd=f_gu + f_dn, bwd=2 * f_gu + 2 * f_dn, total=3 * f_gu + 3 * f_dn)
-
-
-def expected_rows(cfg: LayerConfig) -> float:
-    """Mean number of local rows for unbiased logits: T * k * E_loc / E."""
-    return cfg.T * cfg.k * cfg.E_loc / cfg.E if cfg.bias is None else float("nan")
-
-
-if __name__ == "__main__":  # pragma: no cover - manual inspection
-    for name, c in LAYER_CONFIGS.items():
-        print(name, c, expected_rows(c), math.isnan(expected_rows(c)))

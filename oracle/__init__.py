@@ -34,7 +34,7 @@ Two numeric modes:
 Parity status: every function here is pinned by tests under tests/ (closed forms, limits,
 library special cases, brute force, finite differences, autograd). None is "parity unpinned".
 """
-from .bf16 import bf16_round, bf16_widen, bf16_to_bits
+from .bf16 import bf16_round, bf16_widen
 from .situ import situ_glu_fwd, situ_glu_bwd, situ_parts
 from .route import route_topk
 from .permute import permute
@@ -43,7 +43,7 @@ from .layer import (expert_layer_fwd, expert_layer_bwd, token_layer_fwd, token_l
                     dw_columns, router_bwd, unpermute_sum)
 
 __all__ = [
-    "bf16_round", "bf16_widen", "bf16_to_bits", "situ_glu_fwd", "situ_glu_bwd", "situ_parts",
+    "bf16_round", "bf16_widen", "situ_glu_fwd", "situ_glu_bwd", "situ_parts",
     "route_topk", "permute", "expert_layer_fwd", "expert_layer_bwd", "token_layer_fwd",
     "token_layer_bwd", "dw_columns", "router_bwd", "unpermute_sum",
 ]

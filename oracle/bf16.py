@@ -36,9 +36,3 @@ def bf16_widen(bits) -> np.ndarray:
     """Exact fp64 value of bf16 bit patterns given as uint16."""
     b = np.asarray(bits, dtype=np.uint16)
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
-
-
-def bf16_to_bits(v) -> np.ndarray:
-    """Bit patterns (uint16) of values that already lie on the bf16 grid."""
-    v32 = np.asarray(v, dtype=np.float64).astype(np.float32)
-    return (v32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)

@@ -38,7 +38,9 @@ def expert_layer_fwd(x, w_gu, w_down, perm, H, beta=4.0, linear_beta=25.0, mode=
     """Grouped forward, one local expert at a time.
 
     x [T,d] (bf16 bits or float), w_gu [E_loc,2H,d], w_down [E_loc,d,H], perm from
-    `permute`. Returns dict(y [T,d], h [R,2H], a [R,H]) (h, a only when keep=True).
+    `permute`. Returns dict(y [T,d], y_sum [T,d], h [R,2H], a [R,H]) (h, a only when
+    keep=True); y_sum is the fp64 sum over routes before y's own rounding (y = y_sum in mode
+    "X", y = bf16(y_sum) in mode "S").
     """
     xf = _f64(x)
     T, d = xf.shape
@@ -61,7 +63,7 @@ def expert_layer_fwd(x, w_gu, w_down, perm, H, beta=4.0, linear_beta=25.0, mode=
         if keep:
             h_all[r0:r1] = h
             a_all[r0:r1] = a
-    return dict(y=_maybe_round(y, mode), h=h_all, a=a_all)
+    return dict(y=_maybe_round(y, mode), y_sum=y, h=h_all, a=a_all)
 
 
 def _stored_h(h, h_store):
@@ -75,8 +77,9 @@ def expert_layer_bwd(x, dy, w_gu, w_down, perm, H, beta=4.0, linear_beta=25.0, m
 
     h_store="mxfp8": the saved h went through MXFP8 storage (oracle.mxfp8), so the
     activation and its gradient are recomputed from the stored value.
-    Returns dict(dx [T,d], dw_gu [E_loc,2H,d], dw_down [E_loc,d,H], dp [T,k], dp_rows [R])
-    and dh [R,2H] when keep=True.
+    Returns dict(dx [T,d], dx_sum [T,d], dw_gu [E_loc,2H,d], dw_down [E_loc,d,H], dp [T,k],
+    dp_rows [R]) and dh [R,2H] when keep=True; dx_sum is the fp64 sum over routes before dx's
+    own rounding.
     """
     xf = _f64(x)
     dyf = _f64(dy)
@@ -109,7 +112,7 @@ def expert_layer_bwd(x, dy, w_gu, w_down, perm, H, beta=4.0, linear_beta=25.0, m
         if keep:
             dh_all[r0:r1] = dh
     dp = np.where(slot_row >= 0, dp_rows[np.maximum(slot_row, 0)] if R else 0.0, 0.0)
-    return dict(dx=_maybe_round(dx, mode), dw_gu=dw_gu, dw_down=dw_down, dp=dp,
+    return dict(dx=_maybe_round(dx, mode), dx_sum=dx, dw_gu=dw_gu, dw_down=dw_down, dp=dp,
                 dp_rows=dp_rows, dh=dh_all)
 
 

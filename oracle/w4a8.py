@@ -31,7 +31,8 @@ def expert_layer_fwd_w4a8(x, w_gu, w_down, perm, H, beta=4.0, linear_beta=25.0):
     """Grouped W4A8 forward, one local expert at a time.
 
     x [T,d] (bf16 bits or float), w_gu [E_loc,2H,d], w_down [E_loc,d,H] (full precision;
-    quantized here), perm from `permute`. Returns dict(y [T,d] bf16-rounded, h [R,2H],
+    quantized here), perm from `permute`. Returns dict(y [T,d] bf16-rounded, y_sum [T,d] (the
+    fp64 sum before that rounding), h [R,2H],
     a [R,H], a_codes [R,H], a_scales [R,H/32], h_mag [R,2H]) with h_mag = |x8| . |w4_gu|^T,
     the sum of the magnitudes of the products behind each h (a scale for error bounds). The
     MXFP8 blocks of x run along each token's row, so quantizing the gathered rows of an
@@ -64,5 +65,5 @@ def expert_layer_fwd_w4a8(x, w_gu, w_down, perm, H, beta=4.0, linear_beta=25.0):
         h_all[r0:r1], a_all[r0:r1] = h, a
         h_mag[r0:r1] = np.abs(x8) @ np.abs(wgu4).T
         a_codes[r0:r1], a_scales[r0:r1] = ac, asc
-    return dict(y=bf16_round(y), h=h_all, a=a_all, a_codes=a_codes, a_scales=a_scales,
-                h_mag=h_mag)
+    return dict(y=bf16_round(y), y_sum=y, h=h_all, a=a_all, a_codes=a_codes,
+                a_scales=a_scales, h_mag=h_mag)

@@ -45,6 +45,44 @@ def test_bf16_round_is_direct_from_fp64():
     assert bf16_round(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2 * 2.0 ** -7
 
 
+def test_bf16_widen_matches_torch_on_every_bit_pattern():
+    """All 65,536 bf16 bit patterns widen to the value torch assigns them (its bfloat16 view of
+    the same bits, cast to fp64): zeros of both signs, subnormals, normals, infinities and
+    NaNs. A wrong shift, byte order or view fails here, independently of the oracle's other
+    helpers, which all decode through this function."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.bf16_widen(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert ours.dtype == np.float64 and ours.shape == (1 << 16,)
+    assert np.array_equal(ours, ref, equal_nan=True)
+    assert np.array_equal(np.signbit(ours), np.signbit(ref))
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 * 127 and np.array_equal(np.isnan(ours), nan)
+    # spot values from the format's definition
+    assert ours[0x3F80] == 1.0 and ours[0xBF80] == -1.0 and ours[0x0001] == 2.0 ** -133
+    assert ours[0x7F7F] == (2.0 - 2.0 ** -7) * 2.0 ** 127 and ours[0x7F80] == np.inf
+
+
+def test_layer_sums_are_rounded_once():
+    """The forward's y and the backward's dx are their pre-rounding sums rounded once: in mode
+    S, y = bf16(y_sum) and dx = bf16(dx_sum) exactly; in mode X the sums are the outputs; and
+    the mode-S sums stay within the storage roundings (h, a, dh to bf16) of the exact ones."""
+    cfg = LayerConfig("s", T=40, d=64, H=64, E=6, k=3, e_lo=1, E_loc=4)
+    inp = layer_inputs(cfg, seed=5)
+    idx, gates = route_topk(inp["logits"], cfg.k)
+    perm = permute(idx, gates, cfg.e_lo, cfg.E_loc)
+    fs = expert_layer_fwd(inp["x"], inp["w_gu"], inp["w_down"], perm, cfg.H, mode="S")
+    fx = expert_layer_fwd(inp["x"], inp["w_gu"], inp["w_down"], perm, cfg.H, mode="X")
+    bs = expert_layer_bwd(inp["x"], inp["dy"], inp["w_gu"], inp["w_down"], perm, cfg.H, mode="S")
+    bx = expert_layer_bwd(inp["x"], inp["dy"], inp["w_gu"], inp["w_down"], perm, cfg.H, mode="X")
+    assert np.array_equal(fs["y"], bf16_round(fs["y_sum"]))
+    assert np.array_equal(bs["dx"], bf16_round(bs["dx_sum"]))
+    assert np.array_equal(fx["y"], fx["y_sum"]) and np.array_equal(bx["dx"], bx["dx_sum"])
+    assert not np.array_equal(fs["y_sum"], fs["y"])          # the rounding is not a no-op
+    for s_, x_ in ((fs["y_sum"], fx["y"]), (bs["dx_sum"], bx["dx"])):
+        assert np.max(np.abs(s_ - x_)) <= 2.0 ** -6 * np.max(np.abs(x_))
+
+
 # ----------------------------------------------------------------------------- SiTU-GLU
 def _h(g, l):
     g = np.atleast_1d(np.asarray(g, np.float64))
