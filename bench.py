@@ -2,13 +2,17 @@
 
 A step is one pass of the whole layer over one batch of synthetic input:
   route (top-k + softmax) -> permute -> gate/up GEMM + SiTU-GLU -> down GEMM + combine
-  -> backward (re-dispatch, dA GEMM + SiTU-GLU' + dp, dW_down, dW_gu, dX + combine, dp).
+  -> backward (dA GEMM + SiTU-GLU' + dp partials, dW_down, dW_gu, dX + combine, dp).
 `value` is the layer's useful GEMM throughput, 18 R d H FLOP per step over the measured step
-time (TFLOP/s); the JSON line also carries the standalone streaming SiTU-GLU rate (GB/s) on
-its own workload, the roofline of the dominant kernel, and the fp64 CPU oracle's rate on a
-bounded sample of the same workload.
+time (TFLOP/s), on the large-context workload (98304 tokens dispatched to 28 local experts,
+top-16: R = 1,572,864 routed rows), the largest that fits one GPU. HIP events on the
+library's stream bracket every stage of every timed step; `roofline` is the stage that is one
+kernel and takes the longest. The JSON line also carries the one-rank shard workload as a
+secondary key, the standalone streaming SiTU-GLU rate on its own workload, the MXFP8-store
+and W4A8 variants, peak HBM against the naive six-fp32-copies footprint, and the fp64 CPU
+oracle's rate on a bounded sample of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload shard|large|skew|tiny]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload large|shard|skew|tiny]
 """
 from __future__ import annotations
 
@@ -24,15 +28,22 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE expert fwd+bwd TFLOP/s (% bf16 MFMA peak); SiTU-GLU GB/s (% HBM)"
-# HBM counters of the gate/up GEMM on the shard workload, taken with rocprofv3 (FETCH_SIZE and
-# WRITE_SIZE passes over `bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-situ`, scaled by
-# the same counters over `bench.py --calibrate-copy`). They describe the kernel sources whose
-# digest they record; for any other sources `traffic` is null.
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "gate_up_shard_counters.md")
+PROFILES = os.path.join(ROOT, "profiles")
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (the W4A8 MFMA takes an fp8 operand)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-SHARD_ROWS = 16456             # routed local rows of the shard workload's seed-0 logits
+
+# The stages of one step, in launch order: (name, kernels in it, FLOP per launch as a multiple
+# of R d H). Stages that are one kernel can carry the roofline.
+STAGES = [("route_permute", "route + permute count/scan/scatter", 0.0),
+          ("gate_up", "gate/up GEMM + SiTU-GLU epilogue", 4.0),
+          ("down_combine", "down GEMM + combine", 2.0),
+          ("dA", "dA GEMM + SiTU-GLU' + dp partials", 2.0),
+          ("dW_down", "dW_down GEMM (fp32)", 2.0),
+          ("dW_gu", "dW_gu GEMM (fp32)", 4.0),
+          ("dX_combine", "dX GEMM + combine", 4.0),
+          ("dp", "dp row reduce + scatter", 0.0)]
+SINGLE_KERNEL = ("gate_up", "dA", "dW_down", "dW_gu")
 
 
 def parse():
@@ -40,9 +51,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="shard")
+    ap.add_argument("--workload", default="large")
+    ap.add_argument("--secondary", default="shard",
+                    help="second layer workload reported as an extra key ('none' to skip)")
+    ap.add_argument("--combine-passes", type=int, default=1,
+                    help="passes over the output columns per combine (less fp32 row memory)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-situ", action="store_true")
+    ap.add_argument("--no-variants", action="store_true", help="skip the MXFP8-store and W4A8 legs")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run 3 plain 1 GiB device copies (counter calibration)")
@@ -53,10 +69,59 @@ def parse():
     return ap.parse_args()
 
 
+def kernel_source_digest():
+    """sha256 over the HIP sources and the build flags of the library."""
+    import hashlib
+    pkg = os.path.join(ROOT, "sparse_moe_expert_top_amd")
+    h = hashlib.sha256()
+    files = [os.path.join(pkg, "csrc", f) for f in sorted(os.listdir(os.path.join(pkg, "csrc")))]
+    for f in files + [os.path.join(pkg, "build.py")]:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def committed_traffic(workload, stage):
+    """HBM bytes per launch of a stage's kernel from the committed counter summary
+    profiles/<stage>_<workload>_counters.md, or None when it is missing or was taken on other
+    kernel sources (its source_sha256 must match the current digest)."""
+    path = os.path.join(PROFILES, f"{stage}_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith(("#", "|", " ", "`")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return {"fetch": float(kv["fetch_bytes_per_launch"]),
+                "write": float(kv["write_bytes_per_launch"])}
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy():
+    """Three plain device copies of 1 GiB: FETCH_SIZE / WRITE_SIZE of these dispatches give
+    the counters' scale (bytes per counted KiB)."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
+                      "dispatches": 3}), flush=True)
+
+
 def blas_reference(cfg, R):
     """torch's bf16 GEMMs (hipBLASLt) on dense and per-expert batched forms of the layer's
-    contractions with the shard workload's mean rows per expert; contiguous operands. Context
-    for the grouped kernels' TFLOP/s, not part of the path."""
+    contractions with R rows spread evenly over the experts; contiguous operands. Context for
+    the grouped kernels' TFLOP/s, not part of the path."""
     import torch
     dev = "cuda"
     d, H, E = cfg.d, cfg.H, cfg.E_loc
@@ -89,59 +154,19 @@ def blas_reference(cfg, R):
     print(json.dumps({"blas_reference": out, "rows_per_expert": Re}))
 
 
-def kernel_source_digest():
-    """sha256 over the HIP sources and the build flags of the library."""
-    import hashlib
-    pkg = os.path.join(ROOT, "sparse_moe_expert_top_amd")
-    h = hashlib.sha256()
-    files = [os.path.join(pkg, "csrc", f) for f in sorted(os.listdir(os.path.join(pkg, "csrc")))]
-    for f in files + [os.path.join(pkg, "build.py")]:
-        h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()
-
-
-def committed_traffic(workload):
-    """HBM bytes per gate/up launch from the committed counter summary, or None when the
-    summary is missing, is for another workload, or was taken on other kernel sources."""
-    if workload != "shard" or not os.path.exists(COUNTERS_FILE):
-        return None
-    kv = {}
-    with open(COUNTERS_FILE) as fh:
-        for line in fh:
-            if ":" in line and not line.startswith(("#", "|", " ", "`")):
-                k, v = line.split(":", 1)
-                kv[k.strip()] = v.strip()
-    if kv.get("source_sha256") != kernel_source_digest():
-        return None
-    try:
-        return {"fetch": float(kv["fetch_bytes_per_launch"]),
-                "write": float(kv["write_bytes_per_launch"])}
-    except (KeyError, ValueError):
-        return None
-
-
-def calibrate_copy():
-    """Three plain device copies of 1 GiB: FETCH_SIZE / WRITE_SIZE of these dispatches give
-    the counters' scale (bytes per counted KiB)."""
-    import torch
-    n = 1 << 30
-    src = torch.ones(n, dtype=torch.uint8, device="cuda")
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
-                      "dispatches": 3}), flush=True)
-
-
 def bf16_dev(u16, torch):
     return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).cuda().view(torch.bfloat16)
 
 
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def cpu_baseline(cfg, inp, target_s):
-    """Time the fp64 oracle (as it stands) on the first n local experts of the same input."""
+    """Time the fp64 oracle (as it stands) on a row sample of one expert of the same input:
+    the first n routed rows of local expert 0, run as a layer of those n tokens with that one
+    expert (its rows are independent of the rest). n is sized from a warm timing so the run
+    takes about target_s seconds."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -150,35 +175,111 @@ def cpu_baseline(cfg, inp, target_s):
         threads = len(os.sched_getaffinity(0))
     idx, gates = oracle.route_topk(inp["logits"], cfg.k)
     perm = oracle.permute(idx, gates, cfg.e_lo, cfg.E_loc)
+    off = perm["offsets"]
+    e0 = int(np.argmax(np.diff(off) > 0))                 # first local expert with rows
+    r0, n_e = int(off[e0]), int(off[e0 + 1] - off[e0])
 
     def sub(n):
-        off = perm["offsets"][: n + 1]
-        R = int(off[-1])
-        keep = np.zeros(perm["R"] + 1, bool)
-        keep[:R] = True
-        sr = np.where((perm["slot_row"] >= 0) & (perm["slot_row"] < R), perm["slot_row"], -1)
-        return dict(offsets=off, row_token=perm["row_token"][:R], row_gate=perm["row_gate"][:R],
-                    slot_row=sr.astype(np.int32), R=R)
+        rows = r0 + np.arange(n)
+        tok = perm["row_token"][rows]
+        slot = np.full((n, cfg.k), -1, np.int32)
+        slot[np.arange(n), np.argmax(idx[tok] == cfg.e_lo + e0, axis=1)] = np.arange(n)
+        p = dict(offsets=np.array([0, n], np.int32), row_token=np.arange(n, dtype=np.int32),
+                 row_gate=perm["row_gate"][rows], slot_row=slot, R=n)
+        return p, inp["x"][tok], inp["dy"][tok]
+
+    w_gu, w_down = inp["w_gu"][e0:e0 + 1], inp["w_down"][e0:e0 + 1]
 
     def run(n):
-        p = sub(n)
-        w_gu, w_down = inp["w_gu"][:n], inp["w_down"][:n]
+        p, x, dy = sub(n)
         t0 = time.perf_counter()
-        oracle.expert_layer_fwd(inp["x"], w_gu, w_down, p, cfg.H, mode="S", keep=False)
-        oracle.expert_layer_bwd(inp["x"], inp["dy"], w_gu, w_down, p, cfg.H, mode="S")
-        return time.perf_counter() - t0, p["R"]
+        oracle.expert_layer_fwd(x, w_gu, w_down, p, cfg.H, mode="S", keep=False)
+        oracle.expert_layer_bwd(x, dy, w_gu, w_down, p, cfg.H, mode="S")
+        return time.perf_counter() - t0
 
-    run(1)                                   # first call pays thread-pool and page-in start-up
-    t1, _ = run(1)
-    t2, _ = run(2)
-    per = max(t2 - t1, 1e-3)                 # each call also has a fixed cost (the combine over T)
-    n = int(max(1, min(cfg.E_loc, (target_s - (t1 - per)) / per)))
-    dt, R = run(n)
-    flop = 18.0 * R * cfg.d * cfg.H
+    n0 = min(1024, n_e)
+    run(n0)                                   # first call pays thread-pool and page-in start-up
+    t1 = run(n0)
+    n = int(max(n0, min(n_e, n0 * target_s / max(t1, 1e-3))))
+    dt = run(n)
+    flop = 18.0 * n * cfg.d * cfg.H
     return dict(value=flop / dt / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
-                sample=f"fp64 oracle forward+backward of local experts 0..{n - 1} "
-                       f"({R} routed rows of {perm['R']}) of the same input; {dt:.1f} s",
+                sample=f"fp64 oracle forward+backward of the first {n} routed rows of local "
+                       f"expert {e0} (of {n_e}; {perm['R']} rows in all) of the same input, as "
+                       f"a layer of those {n} tokens; {dt:.1f} s",
                 seconds=round(dt, 2))
+
+
+def load_workload(cfg, torch):
+    from moe_inputs import layer_inputs
+    log(f"generating inputs for {cfg.name}")
+    inp = layer_inputs(cfg, seed=0)
+    t = dict(x=bf16_dev(inp["x"], torch), dy=bf16_dev(inp["dy"], torch),
+             w_gu=bf16_dev(inp["w_gu"], torch), w_down=bf16_dev(inp["w_down"], torch),
+             logits=torch.from_numpy(inp["logits"]).cuda())
+    return inp, t
+
+
+def timed_steps(moe, buf, t, steps, warmup, torch):
+    """W warm-up steps, then `steps` timed steps with HIP events between the stages, on the
+    stream the library launches on. Returns (ms per step from the host clock around the
+    synchronized loop, mean ms per stage)."""
+    stream = torch.cuda.current_stream()
+    bwd = [moe.MOE_BWD_DA, moe.MOE_BWD_DW_DOWN, moe.MOE_BWD_DW_GU, moe.MOE_BWD_DX, moe.MOE_BWD_DP]
+
+    def step(ev):
+        ev[0].record(stream)
+        buf.route(t["logits"])
+        ev[1].record(stream)
+        buf.gate_up(t["x"], t["w_gu"])
+        ev[2].record(stream)
+        buf.down_combine(t["w_down"])
+        ev[3].record(stream)
+        for i, st in enumerate(bwd):
+            buf.backward(t["dy"], t["x"], t["w_gu"], t["w_down"], stages=st)
+            ev[4 + i].record(stream)
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)]
+    for _ in range(warmup):
+        step(mk())
+    torch.cuda.synchronize()
+    evs = [mk() for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    stage_ms = {name: float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in evs]))
+                for j, (name, _, _) in enumerate(STAGES)}
+    return ms_step, stage_ms
+
+
+def layer_leg(moe, cfg, t, steps, warmup, passes, torch, h_store="bf16"):
+    shape = moe.LayerShape(T=cfg.T, E=cfg.E, k=cfg.k, e_lo=cfg.e_lo, E_loc=cfg.E_loc, d=cfg.d,
+                           H=cfg.H, beta=cfg.beta, linear_beta=cfg.linear_beta)
+    R = moe.LayerBuffers.routed_rows(shape, t["logits"])
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    buf = moe.LayerBuffers(shape, R_cap=R, h_store=h_store, combine_passes=passes)
+    ms_step, stage_ms = timed_steps(moe, buf, t, steps, warmup, torch)
+    assert buf.rows() == R and not buf.overflowed()
+    peak = torch.cuda.max_memory_allocated() / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    return R, ms_step, stage_ms, peak
+
+
+def stage_report(stage_ms, R, cfg):
+    rdh = float(R) * cfg.d * cfg.H
+    out = {}
+    for name, what, mult in STAGES:
+        ms = stage_ms[name]
+        e = {"ms": round(ms, 4), "kernels": what}
+        if mult:
+            e["TFLOP/s"] = round(mult * rdh / (ms * 1e-3) / 1e12, 1)
+        out[name] = e
+    return out
 
 
 def main():
@@ -197,77 +298,27 @@ def main():
 
     import torch
     import sparse_moe_expert_top_amd as moe
-    from moe_inputs import LAYER_CONFIGS, SITU_CONFIGS, layer_inputs, situ_inputs
+    from moe_inputs import LAYER_CONFIGS, SITU_CONFIGS, situ_inputs
 
     torch.cuda.set_device(0)
     cfg = LAYER_CONFIGS[args.workload]
     if args.blas_reference:
-        blas_reference(cfg, SHARD_ROWS)
+        blas_reference(cfg, 16456)
         return
-    print(f"[bench] generating inputs for {cfg.name}", file=sys.stderr, flush=True)
-    inp = layer_inputs(cfg, seed=0)
-    x, dy = bf16_dev(inp["x"], torch), bf16_dev(inp["dy"], torch)
-    w_gu, w_down = bf16_dev(inp["w_gu"], torch), bf16_dev(inp["w_down"], torch)
-    logits = torch.from_numpy(inp["logits"]).cuda()
-    shape = moe.LayerShape(T=cfg.T, E=cfg.E, k=cfg.k, e_lo=cfg.e_lo, E_loc=cfg.E_loc, d=cfg.d,
-                           H=cfg.H, beta=cfg.beta, linear_beta=cfg.linear_beta)
-    torch.cuda.reset_peak_memory_stats()
-    buf = moe.LayerBuffers(shape)
-    stream = torch.cuda.current_stream()
+    inp, t = load_workload(cfg, torch)
+    input_gb = sum(v.numel() * v.element_size() for v in t.values()) / 1e9
 
-    print("[bench] warmup", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        buf.step(x, logits, w_gu, w_down, dy)
-    torch.cuda.synchronize()
-    R = buf.rows()
-    assert not buf.overflowed()
-    flop_step = 18.0 * R * cfg.d * cfg.H
-    flop_gu = 4.0 * R * cfg.d * cfg.H
-
-    # timed region: K full steps; HIP events bracket every gate/up GEMM launch on its stream
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        buf.route(logits)
-        ev[i][0].record(stream)
-        moe.moe_grouped_gemm_gate_up(x, buf.perm["row_token"], buf.perm["offsets"], w_gu,
-                                     buf.R_cap, cfg.beta, cfg.linear_beta, h=buf.h, a=buf.a)
-        ev[i][1].record(stream)
-        moe.moe_grouped_gemm_down_combine(buf.a, buf.perm["offsets"], buf.perm["row_gate"],
-                                          buf.perm["slot_row"], w_down, buf.R_cap, y=buf.y,
-                                          ws=buf.ws_down)
-        buf.backward(dy, x, w_gu, w_down)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_step = elapsed * 1e3 / args.steps
-    gu_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-
-    # one more step with events between the phases (breakdown only, not the headline)
-    evs[0].record(stream)
-    buf.route(logits)
-    evs[1].record(stream)
-    moe.moe_grouped_gemm_gate_up(x, buf.perm["row_token"], buf.perm["offsets"], w_gu, buf.R_cap,
-                                 cfg.beta, cfg.linear_beta, h=buf.h, a=buf.a)
-    evs[2].record(stream)
-    moe.moe_grouped_gemm_down_combine(buf.a, buf.perm["offsets"], buf.perm["row_gate"],
-                                      buf.perm["slot_row"], w_down, buf.R_cap, y=buf.y,
-                                      ws=buf.ws_down)
-    evs[3].record(stream)
-    buf.backward(dy, x, w_gu, w_down)
-    evs[4].record(stream)
-    torch.cuda.synchronize()
-    phases = dict(route_permute=evs[0].elapsed_time(evs[1]), gate_up=evs[1].elapsed_time(evs[2]),
-                  down_combine=evs[2].elapsed_time(evs[3]), backward=evs[3].elapsed_time(evs[4]))
-    peak_gb = torch.cuda.max_memory_allocated() / 1e9
-
-    # gate/up moves each local expert's [2H, d] weights once, the R gathered rows of x, and
-    # writes h [R, 2H] and a [R, H]
-    gu_bytes = 2.0 * (cfg.E_loc * 2 * cfg.H * cfg.d + R * cfg.d + R * 3 * cfg.H)
+    log(f"{cfg.name}: {args.warmup} warm-up + {args.steps} timed steps")
+    R, ms_step, stage_ms, peak_gb = layer_leg(moe, cfg, t, args.steps, args.warmup,
+                                              args.combine_passes, torch)
+    rdh = float(R) * cfg.d * cfg.H
+    flop_step = 18.0 * rdh
     value = flop_step / (ms_step * 1e-3) / 1e12
-    gu_tflops = flop_gu / (gu_ms * 1e-3) / 1e12
+    stages = stage_report(stage_ms, R, cfg)
+    dom = max(SINGLE_KERNEL, key=lambda n: stage_ms[n])
+    dom_mult = dict((n, m) for n, _, m in STAGES)[dom]
+    dom_flop = dom_mult * rdh
+    dom_tf = dom_flop / (stage_ms[dom] * 1e-3) / 1e12
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -275,91 +326,115 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.note}; T={cfg.T} d={cfg.d} H={cfg.H} "
                                f"E={cfg.E} k={cfg.k} local experts {cfg.e_lo}..{cfg.e_lo + cfg.E_loc - 1}",
-                   "routed_rows": R, "flop_per_step": flop_step, "row_capacity": buf.R_cap},
+                   "routed_rows": R, "flop_per_step": flop_step, "row_capacity": R,
+                   "combine_passes": args.combine_passes},
         "mfma_frac": round(value / PEAK_BF16_TFLOPS, 4),
-        "roofline": {"kernel": "grouped GEMM gate/up + SiTU-GLU epilogue", "bound": "mfma",
-                     "achieved": round(gu_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4),
-                     "avg_launch_ms": round(gu_ms, 4), "flop_per_launch": flop_gu,
-                     "algorithmic_bytes_per_launch": gu_bytes, "traffic": None},
-        "phase_ms": {k: round(v, 4) for k, v in phases.items()},
+        "roofline": {"kernel": f"{dom}: {dict((n, w) for n, w, _ in STAGES)[dom]}",
+                     "bound": "mfma", "achieved": round(dom_tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
+                     "avg_launch_ms": round(stage_ms[dom], 4), "flop_per_launch": dom_flop,
+                     "traffic": None},
+        "stages": stages,
         "peak_hbm_GB": round(peak_gb, 2),
+        "inputs_and_weights_GB": round(input_gb, 2),
         "saved_activation_GB": round((R * 2 * cfg.H * 2 + cfg.T * cfg.d * 2) / 1e9, 3),
         "naive_saved_fp32_GB": round(6 * R * cfg.H * 4 / 1e9, 3),
     }
-    # the same step with the saved h stored as MXFP8 (E4M3 codes + one scale byte per 32)
-    del buf
-    torch.cuda.empty_cache()
-    bmx = moe.LayerBuffers(shape, h_store="mxfp8")
-    for _ in range(args.warmup):
-        bmx.step(x, logits, w_gu, w_down, dy)
-    torch.cuda.synchronize()
-    n_mx = max(1, args.steps // 2)
-    t0 = time.perf_counter()
-    for _ in range(n_mx):
-        bmx.step(x, logits, w_gu, w_down, dy)
-    torch.cuda.synchronize()
-    ms_mx = (time.perf_counter() - t0) * 1e3 / n_mx
-    out["mxfp8_h"] = {"ms_per_step": round(ms_mx, 4),
-                      "value": round(flop_step / (ms_mx * 1e-3) / 1e12, 2),
-                      "saved_activation_GB": round((R * 2 * cfg.H * (1 + 1 / 32) + cfg.T * cfg.d * 2) / 1e9, 3),
-                      "steps": n_mx}
-    del bmx
-    torch.cuda.empty_cache()
-
-    # W4A8 forward (rollouts): MXFP4 weights quantized once, x quantized to MXFP8 each step
-    print("[bench] W4A8 forward", file=sys.stderr, flush=True)
-    w4 = moe.W4A8Weights(w_gu, w_down)
-    b4 = moe.LayerBuffers(shape)
-    for _ in range(args.warmup):
-        b4.forward_w4a8(x, logits, w4)
-    torch.cuda.synchronize()
-    assert b4.rows() == R
-    ev4 = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        b4.route(logits)
-        moe.moe_mxfp8_quantize(x, codes=b4.x_codes, scales=b4.x_scales)
-        ev4[i][0].record(stream)
-        moe.moe_grouped_gemm_gate_up_w4a8(b4.x_codes, b4.x_scales, b4.perm["row_token"],
-                                          b4.perm["offsets"], w4.gu_codes, w4.gu_scales,
-                                          b4.R_cap, cfg.beta, cfg.linear_beta,
-                                          a_codes=b4.a_codes, a_scales=b4.a_scales)
-        ev4[i][1].record(stream)
-        moe.moe_grouped_gemm_down_combine_w4a8(b4.a_codes, b4.a_scales, b4.perm["offsets"],
-                                               b4.perm["row_gate"], b4.perm["slot_row"],
-                                               w4.down_codes, w4.down_scales, b4.R_cap,
-                                               y=b4.y, ws=b4.ws_down)
-        ev4[i][2].record(stream)
-    torch.cuda.synchronize()
-    ms_w4 = (time.perf_counter() - t0) * 1e3 / args.steps
-    gu4_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev4]))
-    dn4_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev4]))
-    flop_fwd = 6.0 * R * cfg.d * cfg.H
-    out["w4a8_fwd"] = {
-        "ms_per_step": round(ms_w4, 4), "value": round(flop_fwd / (ms_w4 * 1e-3) / 1e12, 2),
-        "unit": "TFLOP/s (forward, 6 R d H)", "steps": args.steps,
-        "bf16_fwd_ms": round(phases["route_permute"] + phases["gate_up"] + phases["down_combine"], 4),
-        "gate_up_ms": round(gu4_ms, 4),
-        "gate_up_TFLOPs": round(flop_gu / (gu4_ms * 1e-3) / 1e12, 2),
-        "gate_up_frac_fp8_peak": round(flop_gu / (gu4_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
-        "down_combine_ms": round(dn4_ms, 4),
-        "weights_GB": round(cfg.E_loc * 3 * cfg.H * cfg.d * (0.5 + 1 / 32) / 1e9, 3),
-        "bf16_weights_GB": round(cfg.E_loc * 3 * cfg.H * cfg.d * 2 / 1e9, 3),
-    }
-    del b4, w4
-    torch.cuda.empty_cache()
-
-    tr = committed_traffic(args.workload)
+    tr = committed_traffic(cfg.name, dom)
     if tr is not None:
-        out["roofline"]["traffic"] = tr["fetch"] + tr["write"]
-        out["roofline"].update(traffic_fetch_bytes=tr["fetch"], traffic_write_bytes=tr["write"],
-                               traffic_vs_algorithmic=round((tr["fetch"] + tr["write"]) / gu_bytes, 3))
+        # algorithmic bytes of the weight-gradient and row GEMMs: each operand once, output once
+        alg = {"gate_up": 2.0 * (cfg.E_loc * 2 * cfg.H * cfg.d + R * cfg.d + R * 3 * cfg.H),
+               "dA": 2.0 * (cfg.E_loc * cfg.d * cfg.H + R * cfg.d + 2 * R * 2 * cfg.H + R * cfg.H) + 4.0 * R,
+               "dW_down": 2.0 * (R * cfg.d + R * cfg.H) + 4.0 * cfg.E_loc * cfg.d * cfg.H,
+               "dW_gu": 2.0 * (R * 2 * cfg.H + R * cfg.d) + 4.0 * cfg.E_loc * 2 * cfg.H * cfg.d}[dom]
+        out["roofline"].update(traffic=tr["fetch"] + tr["write"], traffic_fetch_bytes=tr["fetch"],
+                               traffic_write_bytes=tr["write"],
+                               algorithmic_bytes_per_launch=alg,
+                               traffic_vs_algorithmic=round((tr["fetch"] + tr["write"]) / alg, 3))
+
+    if not args.no_variants:
+        # the same step with the saved h stored as MXFP8 (E4M3 codes + one scale byte per 32)
+        log(f"{cfg.name}: MXFP8-store steps")
+        n_mx = max(1, args.steps // 2)
+        _, ms_mx, _, peak_mx = layer_leg(moe, cfg, t, n_mx, max(1, args.warmup // 2),
+                                         args.combine_passes, torch, h_store="mxfp8")
+        out["mxfp8_h"] = {"ms_per_step": round(ms_mx, 4),
+                          "value": round(flop_step / (ms_mx * 1e-3) / 1e12, 2),
+                          "saved_activation_GB": round((R * 2 * cfg.H * (1 + 1 / 32) + cfg.T * cfg.d * 2) / 1e9, 3),
+                          "peak_hbm_GB": round(peak_mx, 2), "steps": n_mx}
+
+        # W4A8 forward (rollouts): MXFP4 weights quantized once, x quantized to MXFP8 each step
+        log(f"{cfg.name}: W4A8 forward")
+        shape = moe.LayerShape(T=cfg.T, E=cfg.E, k=cfg.k, e_lo=cfg.e_lo, E_loc=cfg.E_loc,
+                               d=cfg.d, H=cfg.H, beta=cfg.beta, linear_beta=cfg.linear_beta)
+        w4 = moe.W4A8Weights(t["w_gu"], t["w_down"])
+        b4 = moe.LayerBuffers(shape, R_cap=R)
+        stream = torch.cuda.current_stream()
+        for _ in range(args.warmup):
+            b4.forward_w4a8(t["x"], t["logits"], w4)
+        torch.cuda.synchronize()
+        ev4 = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            b4.route(t["logits"])
+            moe.moe_mxfp8_quantize(t["x"], codes=b4.x_codes, scales=b4.x_scales)
+            ev4[i][0].record(stream)
+            moe.moe_grouped_gemm_gate_up_w4a8(b4.x_codes, b4.x_scales, b4.perm["row_token"],
+                                              b4.perm["offsets"], w4.gu_codes, w4.gu_scales,
+                                              b4.R_cap, cfg.beta, cfg.linear_beta,
+                                              a_codes=b4.a_codes, a_scales=b4.a_scales)
+            ev4[i][1].record(stream)
+            moe.moe_grouped_gemm_down_combine_w4a8(b4.a_codes, b4.a_scales, b4.perm["offsets"],
+                                                   b4.perm["row_gate"], b4.perm["slot_row"],
+                                                   w4.down_codes, w4.down_scales, b4.R_cap,
+                                                   y=b4.y, ws=b4.ws_down)
+            ev4[i][2].record(stream)
+        torch.cuda.synchronize()
+        ms_w4 = (time.perf_counter() - t0) * 1e3 / args.steps
+        assert b4.rows() == R
+        gu4_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev4]))
+        dn4_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev4]))
+        flop_gu = 4.0 * rdh
+        out["w4a8_fwd"] = {
+            "ms_per_step": round(ms_w4, 4), "value": round(6.0 * rdh / (ms_w4 * 1e-3) / 1e12, 2),
+            "unit": "TFLOP/s (forward, 6 R d H)", "steps": args.steps,
+            "bf16_fwd_ms": round(stage_ms["route_permute"] + stage_ms["gate_up"] + stage_ms["down_combine"], 4),
+            "gate_up_ms": round(gu4_ms, 4),
+            "gate_up_TFLOPs": round(flop_gu / (gu4_ms * 1e-3) / 1e12, 2),
+            "gate_up_frac_fp8_peak": round(flop_gu / (gu4_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+            "down_combine_ms": round(dn4_ms, 4),
+            "weights_GB": round(cfg.E_loc * 3 * cfg.H * cfg.d * (0.5 + 1 / 32) / 1e9, 3),
+            "bf16_weights_GB": round(cfg.E_loc * 3 * cfg.H * cfg.d * 2 / 1e9, 3),
+        }
+        del b4, w4
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        log("CPU oracle baseline")
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    del inp, t
+    torch.cuda.empty_cache()
+
+    if args.secondary != "none" and args.secondary != cfg.name:
+        c2 = LAYER_CONFIGS[args.secondary]
+        _, t2 = load_workload(c2, torch)
+        log(f"{c2.name}: {args.warmup} warm-up + {args.steps} timed steps")
+        R2, ms2, st2, peak2 = layer_leg(moe, c2, t2, args.steps, args.warmup,
+                                        args.combine_passes, torch)
+        out[c2.name] = {"workload": f"{c2.name}: {c2.note}", "routed_rows": R2,
+                        "ms_per_step": round(ms2, 4),
+                        "value": round(18.0 * R2 * c2.d * c2.H / (ms2 * 1e-3) / 1e12, 2),
+                        "unit": "TFLOP/s", "stages": stage_report(st2, R2, c2),
+                        "peak_hbm_GB": round(peak2, 2),
+                        "naive_saved_fp32_GB": round(6 * R2 * c2.H * 4 / 1e9, 3)}
+        del t2
+        torch.cuda.empty_cache()
 
     if not args.no_situ:
         sc = SITU_CONFIGS["situ"]
         Rs, Hs = sc["R"], sc["H"]
-        print("[bench] SiTU-GLU streaming", file=sys.stderr, flush=True)
+        log("SiTU-GLU streaming")
+        stream = torch.cuda.current_stream()
         si = situ_inputs(Rs, Hs, seed=0, h_std=sc["h_std"])
         h, da = bf16_dev(si["h"], torch), bf16_dev(si["da"], torch)
         a = torch.empty((Rs, Hs), dtype=torch.bfloat16, device="cuda")
@@ -389,9 +464,6 @@ def main():
         del h, da, a, dh, flush
         torch.cuda.empty_cache()
 
-    if not args.no_cpu_baseline:
-        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

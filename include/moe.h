@@ -27,8 +27,8 @@
  *     hipError_t of the failed launch on the calling thread.
  *   - Pointers to bf16/fp32 tensors must be 16-byte aligned; d and H must be multiples of
  *     64; k <= 32; E <= 1024; E_loc <= 1024. Token-indexed tensors must span less than
- *     4 GiB per row block: T * max(d, 2H) * 2 < 2^32 (checked where T is an argument; for
- *     moe_grouped_gemm_gate_up it is a precondition on x).
+ *     4 GiB per row block: T * max(d, 2H) * 2 < 2^32 (every call that reads token rows
+ *     takes T and checks it before any launch).
  *   - Routed rows R are data-dependent and stay on the device in expert_offsets[E_loc].
  *     Buffers indexed by rows are sized by a caller-chosen capacity R_cap (T*k always
  *     suffices). moe_permute clamps the offsets to R_cap and raises *status_flag when the
@@ -62,8 +62,8 @@ typedef enum {
   MOE_WS_PERMUTE = 1,
   MOE_WS_SITU_GLU_FWD = 2,
   MOE_WS_SITU_GLU_BWD = 3,
-  MOE_WS_DOWN_COMBINE = 4,
-  MOE_WS_EXPERT_BWD = 5
+  MOE_WS_DOWN_COMBINE = 4,      /* one combine pass over all d columns (fastest) */
+  MOE_WS_EXPERT_BWD = 5         /* one dX combine pass over all d columns (fastest) */
 } moe_ws_kind;
 
 /* Static, NUL-terminated description of a status code. Never NULL. */
@@ -110,35 +110,57 @@ moe_status moe_permute(const int32_t* topk_idx, const float* gates, int64_t T, i
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * moe_unpermute - combine: out[t, :] = bf16( sum over j with slot_row[t,j] >= 0 of
- * w(r) * rows[r, :] ), r = slot_row[t, j], w = row_weight[r] or 1 when row_weight is NULL;
- * the sum is taken in fp32 in slot order. Tokens with no local route get zeros.
- *   rows [R_cap, n] bf16, slot_row [T, k] int32, row_weight [R_cap] fp32 or NULL,
- *   out [T, n] bf16. n must be a multiple of 8.
+ * moe_unpermute - combine of expert rows back to tokens: the sum over a token's routes in
+ * the forward equation y = sum_e p_e o_e ("Kimi K3 ... Memory", section "MoE 反向"), and
+ * the return of the re-dispatched rows to their tokens in the backward (same section,
+ * second saving):
+ *   out[t, :] = bf16( sum over j with slot_row[t,j] >= 0 of w(r) * rows[r, :] ),
+ *   r = slot_row[t, j], w = row_weight[r] or 1 when row_weight is NULL; the sum is taken in
+ *   fp32 in slot order. Tokens with no local route get zeros.
+ *   rows [R_cap, n] bf16 (caller-owned, read only), slot_row [T, k] int32, row_weight
+ *   [R_cap] fp32 or NULL, out [T, n] bf16 (written). n must be a multiple of 8; rows and out
+ *   16-byte aligned. Every slot_row entry must be -1 or a row below R_cap (precondition).
+ * Errors: T < 0, k < 1, n < 1 (MOE_ERR_SHAPE); k > 32, n % 8, T * k >= 2^31, misaligned
+ * pointers (MOE_ERR_UNSUPPORTED); NULL pointers when T > 0 (MOE_ERR_NULL).
  */
 moe_status moe_unpermute(const void* rows, const int32_t* slot_row, const float* row_weight,
                          int64_t T, int k, int n, void* out, hipStream_t stream);
 
 /*
- * moe_grouped_gemm_gate_up - for every local expert e and its rows r:
+ * moe_grouped_gemm_gate_up - the expert forward's first half, a_e = SiTU(W_gate x, W_up x)
+ * ("Kimi K3 ... Memory", section "MoE 反向", forward equation), keeping only the bf16
+ * pre-activation for the backward ("Frontier-scale RL with Kimi K3", section "Streaming
+ * activations": the custom op saves one bf16 [R, 2H] tensor). For every local expert e and
+ * its rows r:
  *   h[r, :]  = bf16( x[row_token[r], :] . w_gu[e]^T )           (saved for the backward)
  *   a[r, j]  = bf16( SiTU-GLU(h[r, j], h[r, H + j]) ), j < H      (input of the down GEMM)
  * The dispatch (row gather through row_token) is fused into the operand load; SiTU-GLU is
  * fused into the epilogue and computed in fp32 from the bf16-rounded h.
- *   x [T, d] bf16, row_token [R_cap], expert_offsets [E_loc+1] (device), w_gu
- *   [E_loc, 2H, d] bf16, h [R_cap, 2H] bf16 out, a [R_cap, H] bf16 out.
+ *   x [T, d] bf16 (read), row_token [R_cap] and expert_offsets [E_loc+1] (device, from
+ *   moe_permute), w_gu [E_loc, 2H, d] bf16 (read), h [R_cap, 2H] bf16 and a [R_cap, H] bf16
+ *   (written for rows below expert_offsets[E_loc]; other rows untouched). All caller-owned.
+ * Errors: T < 0, E_loc < 1, R_cap < 0, beta or linear_beta not > 0 (MOE_ERR_SHAPE);
+ * T * max(d, 2H) * 2 >= 2^32 (the gather addresses token rows with 32-bit offsets), d or H
+ * not a multiple of 64, E_loc > 1024, R_cap >= 2^31, misaligned pointers
+ * (MOE_ERR_UNSUPPORTED); NULL pointers (MOE_ERR_NULL). Nothing is launched on error.
  */
-moe_status moe_grouped_gemm_gate_up(const void* x, const int32_t* row_token,
+moe_status moe_grouped_gemm_gate_up(const void* x, int64_t T, const int32_t* row_token,
                                     const int32_t* expert_offsets, int E_loc, int64_t R_cap,
                                     int d, int H, const void* w_gu, float beta,
                                     float linear_beta, void* h, void* a, hipStream_t stream);
 
 /*
- * situ_glu_fwd - streaming SiTU-GLU: a[r, j] = bf16(gate'(h[r, j]) * lin'(h[r, H + j])).
- *   h [R, 2H] bf16, a [R, H] bf16 out. fp32 math in registers; the kernel needs no memory
- *   beyond its inputs and outputs, so `ws` may be NULL and moe_workspace_size reports 0
- *   (the constant-size fp32 working set is the per-wave register tile, independent of R).
- * H must be a multiple of 8.
+ * situ_glu_fwd - streaming SiTU-GLU forward, the naive activation's definition in
+ * "Frontier-scale RL with Kimi K3", section "Streaming activations": the last dimension of h
+ * splits into a gate half g and a linear half l, gate' = beta tanh(g/beta) sigmoid(g),
+ * lin' = linear_beta tanh(l/linear_beta), and the product is cast back to the input dtype:
+ *   a[r, j] = bf16(gate'(h[r, j]) * lin'(h[r, H + j])).
+ *   h [R, 2H] bf16 (read), a [R, H] bf16 (written); caller-owned, 16-byte aligned. fp32
+ *   math in registers; the kernel needs no memory beyond its inputs and outputs, so `ws` may
+ *   be NULL and moe_workspace_size reports 0 (the constant-size fp32 working set is the
+ *   per-wave register tile, independent of R).
+ * Errors: R < 0, H < 1, beta or linear_beta not > 0 (MOE_ERR_SHAPE); H % 8, misaligned
+ * pointers (MOE_ERR_UNSUPPORTED); NULL h or a when R > 0 (MOE_ERR_NULL).
  */
 moe_status situ_glu_fwd(const void* h, int64_t R, int H, float beta, float linear_beta,
                         void* a, void* ws, size_t ws_bytes, hipStream_t stream);
@@ -155,9 +177,15 @@ moe_status situ_glu_bwd(const void* h, const void* da, int64_t R, int H, float b
 /*
  * moe_grouped_gemm_down_combine - o[r, :] = a[r, :] . w_down[e]^T for the rows of each
  * local expert, then y[t, :] = bf16( sum_j p_j o[slot_row[t, j], :] ) ("MoE 反向", forward
- * equation). o is a transient of this call (bf16(p o) rows in `ws`), never kept.
+ * equation). o is a transient of this call, never kept: the fp32 rows p o live in `ws`, and
+ * the combine adds them in fp32 in slot order, so each element of y is rounded to bf16 once.
  *   a [R_cap, H] bf16, row_gate [R_cap] fp32, slot_row [T, k], w_down [E_loc, d, H] bf16,
- *   y [T, d] bf16 out, ws of moe_workspace_size(MOE_WS_DOWN_COMBINE, ...) bytes.
+ *   y [T, d] bf16 out.
+ *   ws: moe_workspace_size(MOE_WS_DOWN_COMBINE, ...) bytes (fp32 rows [R_cap, d]) runs one
+ *   pass; a smaller ws (down to moe_workspace_size_passes with passes = d / 256) runs the
+ *   GEMM and combine once per window of w output columns, w = the largest multiple of 256
+ *   whose fp32 rows [R_cap, w] fit. Results are bit-identical for every ws size.
+ * Errors: as moe_expert_bwd for the shared arguments; MOE_ERR_WORKSPACE below the minimum.
  */
 moe_status moe_grouped_gemm_down_combine(const void* a, const int32_t* expert_offsets,
                                          const float* row_gate, const int32_t* slot_row,
@@ -178,7 +206,16 @@ moe_status moe_grouped_gemm_down_combine(const void* a, const int32_t* expert_of
  * Experts with no rows get dw = 0.
  *   dy, x [T, d] bf16; h [R_cap, 2H] bf16 (saved by the forward); metadata from
  *   moe_permute; dx [T, d] bf16 out; dw_gu [E_loc, 2H, d] fp32 out; dw_down [E_loc, d, H]
- *   fp32 out; dp [T, k] fp32 out; ws of moe_workspace_size(MOE_WS_EXPERT_BWD, ...) bytes.
+ *   fp32 out; dp [T, k] fp32 out.
+ *   ws: dh [R_cap, 2H] bf16, the dp partials and an overlay of bf16(p a) [R_cap, H] with the
+ *   fp32 dX rows. moe_workspace_size(MOE_WS_EXPERT_BWD, ...) bytes combine dx in one pass;
+ *   a smaller ws (down to moe_workspace_size_passes with passes = d / 256) runs the dX GEMM
+ *   and its combine once per window of output columns (bit-identical results).
+ *   dx is summed in fp32 over a token's slots and rounded to bf16 once.
+ * Errors: T < 0, k < 1, E_loc < 1, R_cap < 0, beta or linear_beta not > 0 (MOE_ERR_SHAPE);
+ * k > 32, E_loc > 1024, d or H not a multiple of 64, R_cap >= 2^31, T * k >= 2^31,
+ * T * max(d, 2H) * 2 >= 2^32, misaligned pointers (MOE_ERR_UNSUPPORTED); NULL pointers
+ * (MOE_ERR_NULL); ws below the minimum (MOE_ERR_WORKSPACE).
  */
 moe_status moe_expert_bwd(const void* dy, const void* x, const void* h,
                           const int32_t* row_token, const float* row_gate,
@@ -187,6 +224,37 @@ moe_status moe_expert_bwd(const void* dy, const void* x, const void* h,
                           const void* w_gu, const void* w_down, float beta, float linear_beta,
                           void* dx, float* dw_gu, float* dw_down, float* dp,
                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Stages of the backward, in the order they run (moe_expert_bwd_stages). */
+typedef enum {
+  MOE_BWD_DA = 1,        /* dA GEMM + SiTU-GLU' + dp partials: writes dh, bf16(p a), partials */
+  MOE_BWD_DW_DOWN = 2,   /* dw_down from dy and bf16(p a) */
+  MOE_BWD_DW_GU = 4,     /* dw_gu from dh and x */
+  MOE_BWD_DX = 8,        /* dX GEMM + combine into dx (reuses the memory of bf16(p a)) */
+  MOE_BWD_DP = 16,       /* dp from the partials */
+  MOE_BWD_ALL = 31
+} moe_bwd_stage;
+
+/*
+ * moe_expert_bwd_stages - the stages of moe_expert_bwd selected by the bit mask `stages`,
+ * run in the order of moe_bwd_stage. Calls over one backward must pass the same arguments and
+ * `ws`; the workspace carries what MOE_BWD_DA writes to the later stages, so DA runs first,
+ * and DW_DOWN runs before DX (DX reuses the memory DW_DOWN reads). Running the stages in any
+ * grouping, in that order, gives results bit-identical to moe_expert_bwd; a caller may defer
+ * the weight-gradient GEMMs or time each stage. The saved h is given either as bf16 `h` or as
+ * MXFP8 `h_codes` and `h_scales` (the other form NULL).
+ * Errors: as moe_expert_bwd; stages outside 1..MOE_BWD_ALL or both forms of h given
+ * (MOE_ERR_SHAPE).
+ */
+moe_status moe_expert_bwd_stages(const void* dy, const void* x, const void* h,
+                                 const void* h_codes, const void* h_scales,
+                                 const int32_t* row_token, const float* row_gate,
+                                 const int32_t* slot_row, const int32_t* expert_offsets,
+                                 int64_t T, int k, int E_loc, int64_t R_cap, int d, int H,
+                                 const void* w_gu, const void* w_down, float beta,
+                                 float linear_beta, void* dx, float* dw_gu, float* dw_down,
+                                 float* dp, void* ws, size_t ws_bytes, int stages,
+                                 hipStream_t stream);
 
 /*
  * MXFP8 storage of the saved pre-activation ("Kimi K3 ... Memory", unified activation
@@ -206,7 +274,7 @@ moe_status moe_expert_bwd(const void* dy, const void* x, const void* h,
  *   the bf16 h that `a` is computed from; a [R_cap, H] bf16 out as in the bf16 call.
  * Same arguments, limits and errors otherwise; h_codes must be 16-byte aligned.
  */
-moe_status moe_grouped_gemm_gate_up_mx(const void* x, const int32_t* row_token,
+moe_status moe_grouped_gemm_gate_up_mx(const void* x, int64_t T, const int32_t* row_token,
                                        const int32_t* expert_offsets, int E_loc, int64_t R_cap,
                                        int d, int H, const void* w_gu, float beta,
                                        float linear_beta, void* h_codes, void* h_scales,
@@ -304,8 +372,8 @@ moe_status moe_grouped_gemm_gate_up_w4a8(const void* x_codes, const void* x_scal
  * o[r, :] = a8[r, :] . w4_down[e]^T, y[t, :] = bf16( sum_j p_j o[slot_row[t, j], :] ).
  *   a_codes [R_cap, H], a_scales [R_cap, H/32] from moe_grouped_gemm_gate_up_w4a8;
  *   w_down_codes [E_loc, d, H/2], w_down_scales [E_loc, d, H/32] (moe_mxfp4_quantize of
- *   w_down viewed as [E_loc * d, H]); y [T, d] bf16 out; ws of
- *   moe_workspace_size(MOE_WS_DOWN_COMBINE, ...) bytes (bf16(p o) rows).
+ *   w_down viewed as [E_loc * d, H]); y [T, d] bf16 out; ws as for
+ *   moe_grouped_gemm_down_combine (fp32 rows p o, one pass per window of output columns).
  * Alignment: a_codes, w_down_codes, y, ws 16 bytes; a_scales, w_down_scales 4 bytes.
  * Errors: as moe_grouped_gemm_down_combine.
  */
@@ -323,6 +391,17 @@ moe_status moe_grouped_gemm_down_combine_w4a8(const void* a_codes, const void* a
  */
 moe_status moe_workspace_size(int which, int64_t T, int E_loc, int k, int d, int H,
                               int64_t R_cap, size_t* bytes);
+
+/*
+ * moe_workspace_size_passes - bytes of `ws` for MOE_WS_DOWN_COMBINE (also the W4A8 down
+ * combine) or MOE_WS_EXPERT_BWD (also the MXFP8-store backward) when the combine is to run in
+ * `passes` passes over the output columns: windows of w = ceil(d / passes) rounded up to a
+ * multiple of 256 (at most d) columns. passes = 1 equals moe_workspace_size; fewer bytes per
+ * pass trade fp32 row memory for re-reading the GEMM's row operand once per pass.
+ * Errors: passes < 1 or another `which` (MOE_ERR_SHAPE); as moe_workspace_size otherwise.
+ */
+moe_status moe_workspace_size_passes(int which, int64_t T, int E_loc, int k, int d, int H,
+                                     int64_t R_cap, int passes, size_t* bytes);
 
 #ifdef __cplusplus
 }

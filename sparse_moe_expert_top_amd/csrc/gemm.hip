@@ -36,10 +36,12 @@
 //    GROUP_M super-rows (all n-tiles of group_m m-tiles, m fastest), and consecutive tile
 //    ids go to one XCD (workgroup i runs on XCD i mod 8), so tiles running together on an
 //    XCD share both operand panels in its L2.
-//  * Epilogues: gate_up writes h (bf16) and a = bf16(SiTU-GLU(bf16 h)); down writes
-//    bf16(p * o) rows for the combine; dA recomputes a from the saved h, accumulates the
-//    per-row <G, a> partials, and writes dh and bf16(p a); dX writes bf16 rows; the weight
-//    gradients write fp32 rows (zeros for experts without rows) with streaming stores.
+//  * Epilogues: gate_up writes h (bf16) and a = bf16(SiTU-GLU(bf16 h)); down writes fp32
+//    p * o rows for the combine; dA recomputes a from the saved h, accumulates the per-row
+//    <G, a> partials, and writes dh and bf16(p a); dX writes fp32 rows; the weight gradients
+//    write fp32 rows (zeros for experts without rows) with streaming stores. down and dX
+//    cover a window [c0, c0 + nc) of their output columns per launch, so a caller with a
+//    smaller workspace combines the columns in several passes.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -174,7 +176,9 @@ __device__ __forceinline__ void st_row16(uint16_t* p, u32x4 v) {
 #endif
 }
 
-template <class C, bool KRAG, int BKIND, int EPI>
+// TAG only tells apart contractions that would otherwise share one instantiation (dW_down and
+// dW_gu), so profiles name each kernel.
+template <class C, bool KRAG, int BKIND, int EPI, int TAG = 0>
 __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, NS = C::NS, NT = C::NT, NW = NT / 64;
   constexpr int WM = BM / C::WGM, WN = BN / C::WGN;
@@ -675,14 +679,18 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
           const f32x4 c1 = *(const f32x4*)&st[row * EPS + cc * 8 + 4];
           const float cv[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
           if constexpr (EPI == EPI_ROWS || EPI == EPI_ROWS_SCALED) {
+            // fp32 rows: the combine sums them in fp32 and rounds the token's sum once
             if (rblk + row < Me && col < p.N) {
               const int64_t r = r0 + rblk + row;
-              float sc = 1.0f;
-              if constexpr (EPI == EPI_ROWS_SCALED) sc = rsc[ps];
-              u32x4 o;
-#pragma unroll
-              for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(cv[2 * q] * sc, cv[2 * q + 1] * sc);
-              st_row16(&p.o0[r * p.ld0 + col], o);
+              float* dst = p.of + r * p.ldf + col;
+              if constexpr (EPI == EPI_ROWS_SCALED) {
+                const float sc = rsc[ps];
+                *(f32x4*)dst = f32x4{cv[0] * sc, cv[1] * sc, cv[2] * sc, cv[3] * sc};
+                *(f32x4*)(dst + 4) = f32x4{cv[4] * sc, cv[5] * sc, cv[6] * sc, cv[7] * sc};
+              } else {
+                *(f32x4*)dst = c0;
+                *(f32x4*)(dst + 4) = c1;
+              }
             }
           } else if constexpr (IS_DA) {
             if (rblk + row < Me && col < p.N) {
@@ -765,9 +773,9 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
 }
 
 // ---------------------------------------------------------------------------- launchers
-template <class C, bool KRAG, int BKIND, int EPI>
+template <class C, bool KRAG, int BKIND, int EPI, int TAG = 0>
 static hipError_t run_gemm(const GemmArgs& args, int64_t max_tiles, hipStream_t s) {
-  auto kern = grouped_gemm_kernel<C, KRAG, BKIND, EPI>;
+  auto kern = grouped_gemm_kernel<C, KRAG, BKIND, EPI, TAG>;
   static int occ = -1;                   // workgroups per CU for this instantiation
   if (occ < 0) {
     int o = 0;
@@ -855,15 +863,15 @@ hipError_t launch_gemm_gate_up_mx(const uint16_t* x, const int32_t* row_token,
 }
 
 hipError_t launch_gemm_down(const uint16_t* a, const int32_t* offsets, const float* row_gate,
-                            int E_loc, int64_t R_cap, int H, int d, const uint16_t* w_down,
-                            uint16_t* rows_out, hipStream_t s) {
+                            int E_loc, int64_t R_cap, int H, int d, int c0, int nc,
+                            const uint16_t* w_down, float* rows_out, hipStream_t s) {
   GemmArgs p = blank_args();
   p.A = a; p.lda = H;
-  p.B = w_down; p.ldb = H; p.b_gstride = (int64_t)d * H;
+  p.B = w_down + (int64_t)c0 * H; p.ldb = H; p.b_gstride = (int64_t)d * H;   // rows c0..c0+nc
   p.offsets = offsets; p.G = E_loc;
-  p.N = d; p.K = H;
-  p.n_tiles = (d + CDN::BN - 1) / CDN::BN;
-  p.o0 = rows_out; p.ld0 = d; p.row_scale = row_gate;
+  p.N = nc; p.K = H;
+  p.n_tiles = (nc + CDN::BN - 1) / CDN::BN;
+  p.of = rows_out; p.ldf = nc; p.row_scale = row_gate;
   return run_gemm<CDN, false, B_ROWS, EPI_ROWS_SCALED>(
       p, mragged_tile_bound(R_cap, E_loc, CDN::BM, p.n_tiles), s);
 }
@@ -893,15 +901,15 @@ hipError_t launch_gemm_da(const uint16_t* dy, const int32_t* row_token, const in
 }
 
 hipError_t launch_gemm_dx(const uint16_t* dh, const int32_t* offsets, int E_loc,
-                          int64_t R_cap, int d, int H, const uint16_t* w_gu,
-                          uint16_t* rows_out, hipStream_t s) {
+                          int64_t R_cap, int d, int H, int c0, int nc, const uint16_t* w_gu,
+                          float* rows_out, hipStream_t s) {
   GemmArgs p = blank_args();
   p.A = dh; p.lda = 2 * H;
-  p.B = w_gu; p.ldb = d; p.b_gstride = (int64_t)2 * H * d;    // B(n, k) = w_gu[e][k][n]
+  p.B = w_gu + c0; p.ldb = d; p.b_gstride = (int64_t)2 * H * d;   // B(n, k) = w_gu[e][k][c0 + n]
   p.offsets = offsets; p.G = E_loc;
-  p.N = d; p.K = 2 * H;
-  p.n_tiles = (d + CDX::BN - 1) / CDX::BN;
-  p.o0 = rows_out; p.ld0 = d;
+  p.N = nc; p.K = 2 * H;
+  p.n_tiles = (nc + CDX::BN - 1) / CDX::BN;
+  p.of = rows_out; p.ldf = nc;
   return run_gemm<CDX, false, B_KOUT, EPI_ROWS>(
       p, mragged_tile_bound(R_cap, E_loc, CDX::BM, p.n_tiles), s);
 }
@@ -931,7 +939,7 @@ hipError_t launch_gemm_dw_gu(const uint16_t* dh, const uint16_t* x, const int32_
   p.m_tiles = (2 * H + CWG::BM - 1) / CWG::BM;
   p.n_tiles = (d + CWG::BN - 1) / CWG::BN;
   p.of = dw_gu; p.ldf = d; p.f_gstride = (int64_t)2 * H * d;
-  return run_gemm<CWG, true, B_KOUT, EPI_F32>(p, (int64_t)E_loc * p.m_tiles * p.n_tiles, s);
+  return run_gemm<CWG, true, B_KOUT, EPI_F32, 1>(p, (int64_t)E_loc * p.m_tiles * p.n_tiles, s);
 }
 
 }  // namespace moe

@@ -13,7 +13,8 @@
 //   down      a8[r] . w4_down[e]^T        rows   d    H    a rows             w_down rows
 //
 // gate_up's epilogue rounds h to bf16, applies SiTU-GLU, rounds a to bf16 and writes it as
-// MXFP8 (the down GEMM's A operand); down's writes bf16(p o) rows for the combine.
+// MXFP8 (the down GEMM's A operand); down's writes fp32 p o rows for the combine, over a
+// window of its output columns per launch.
 //
 // Design (gfx950):
 //  * v_mfma_scale_f32_32x32x64_f8f6f4 with A = E4M3, B = E2M1 and fp32 accumulators. Operand
@@ -60,7 +61,9 @@ struct W4A8Args {
   int n_tiles, group_m;
   uint8_t* qa;               // gate_up: a codes [R, H] and scale bytes [R, H/32]
   uint8_t* sa;
-  uint16_t* o;               // down: bf16(p o) rows [R, N]
+  int64_t b_gs, bs_gs;       // per-expert strides of B and Bs (bytes)
+  float* o;                  // down: fp32 p o rows [R, N], leading dimension ldo
+  int64_t ldo;
   const float* row_scale;
   SituCoef sc;
 };
@@ -126,8 +129,8 @@ __global__ __launch_bounds__(512, 2) void w4a8_gemm_kernel(W4A8Args p) {
     balanced_rows<BM>(mt, Mg, m0, Me);
     const int n0 = nt * BN;
     const int j0 = nt * (BN / 2);                  // gate_up: first gate/linear column pair
-    const uint8_t* Bg = p.B + (int64_t)g * p.N * (p.K / 2);
-    const uint8_t* Bsg = p.Bs + (int64_t)g * p.N * ks;
+    const uint8_t* Bg = p.B + (int64_t)g * p.b_gs;
+    const uint8_t* Bsg = p.Bs + (int64_t)g * p.bs_gs;
 
     // weight row of tile row `row` (gate_up interleaves each wavefront's 64 gate rows with
     // the matching 64 linear rows)
@@ -364,12 +367,9 @@ __global__ __launch_bounds__(512, 2) void w4a8_gemm_kernel(W4A8Args p) {
             if (rblk + row < Me && col < p.N) {
               const int64_t r = r0 + rblk + row;
               const float sc = rsc[ps];
-              u32x4 o;
-              o[0] = pack_bf16x2(c0[0] * sc, c0[1] * sc);
-              o[1] = pack_bf16x2(c0[2] * sc, c0[3] * sc);
-              o[2] = pack_bf16x2(c1[0] * sc, c1[1] * sc);
-              o[3] = pack_bf16x2(c1[2] * sc, c1[3] * sc);
-              *(u32x4*)&p.o[r * p.N + col] = o;
+              float* dst = p.o + r * p.ldo + col;
+              *(f32x4*)dst = f32x4{c0[0] * sc, c0[1] * sc, c0[2] * sc, c0[3] * sc};
+              *(f32x4*)(dst + 4) = f32x4{c1[0] * sc, c1[1] * sc, c1[2] * sc, c1[3] * sc};
             }
           }
         }
@@ -415,6 +415,7 @@ hipError_t launch_w4a8_gate_up(const uint8_t* x_codes, const uint8_t* x_scales,
   p.A = x_codes; p.As = x_scales; p.a_gather = row_token;
   p.B = w_codes; p.Bs = w_scales; p.offsets = offsets;
   p.G = E_loc; p.N = 2 * H; p.K = d; p.H = H;
+  p.b_gs = (int64_t)2 * H * (d / 2); p.bs_gs = (int64_t)2 * H * (d / 32);
   p.n_tiles = (H + 127) / 128; p.group_m = MOE_GROUP_M;
   p.qa = a_codes; p.sa = a_scales; p.sc = c;
   return run_w4a8<W4_GATEUP>(p, w4_tile_bound(R_cap, E_loc, p.n_tiles), s);
@@ -422,15 +423,19 @@ hipError_t launch_w4a8_gate_up(const uint8_t* x_codes, const uint8_t* x_scales,
 
 hipError_t launch_w4a8_down(const uint8_t* a_codes, const uint8_t* a_scales,
                             const int32_t* offsets, const float* row_gate, int E_loc,
-                            int64_t R_cap, int H, int d, const uint8_t* w_codes,
-                            const uint8_t* w_scales, uint16_t* rows_out, hipStream_t s) {
+                            int64_t R_cap, int H, int d, int c0, int nc,
+                            const uint8_t* w_codes, const uint8_t* w_scales, float* rows_out,
+                            hipStream_t s) {
   W4A8Args p;
   __builtin_memset(&p, 0, sizeof(p));
   p.A = a_codes; p.As = a_scales;
-  p.B = w_codes; p.Bs = w_scales; p.offsets = offsets;
-  p.G = E_loc; p.N = d; p.K = H; p.H = H;
-  p.n_tiles = (d + 255) / 256; p.group_m = MOE_GROUP_M;
-  p.o = rows_out; p.row_scale = row_gate;
+  // weight rows c0 .. c0 + nc of every expert
+  p.B = w_codes + (int64_t)c0 * (H / 2); p.Bs = w_scales + (int64_t)c0 * (H / 32);
+  p.b_gs = (int64_t)d * (H / 2); p.bs_gs = (int64_t)d * (H / 32);
+  p.offsets = offsets;
+  p.G = E_loc; p.N = nc; p.K = H; p.H = H;
+  p.n_tiles = (nc + 255) / 256; p.group_m = MOE_GROUP_M;
+  p.o = rows_out; p.ldo = nc; p.row_scale = row_gate;
   return run_w4a8<W4_ROWS_SCALED>(p, w4_tile_bound(R_cap, E_loc, p.n_tiles), s);
 }
 

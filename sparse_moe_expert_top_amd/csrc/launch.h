@@ -20,8 +20,14 @@ hipError_t launch_permute(const int32_t* idx, const float* gates, int64_t T, int
                           int E_loc, int64_t R_cap, int32_t* offsets, int32_t* row_token,
                           float* row_gate, int32_t* slot_row, int32_t* status, void* ws,
                           hipStream_t s);
-hipError_t launch_unpermute(const uint16_t* rows, const int32_t* slot_row, const float* w,
-                            int64_t T, int k, int n, uint16_t* out, hipStream_t s);
+// out[t, 0..n) = bf16(sum over local slots of w(r) rows[r, 0..n)), summed in fp32 in slot
+// order; rows have leading dimension ldr (elements), out ldo. n a multiple of 8.
+hipError_t launch_unpermute(const uint16_t* rows, int64_t ldr, const int32_t* slot_row,
+                            const float* w, int64_t T, int k, int n, uint16_t* out,
+                            int64_t ldo, hipStream_t s);
+hipError_t launch_unpermute_f32(const float* rows, int64_t ldr, const int32_t* slot_row,
+                                int64_t T, int k, int n, uint16_t* out, int64_t ldo,
+                                hipStream_t s);
 hipError_t launch_dp_reduce_scatter(float* part, int nslots, int64_t R_cap,
                                     const int32_t* offsets, int E_loc,
                                     const int32_t* slot_row, int64_t T, int k, float* dp,
@@ -46,9 +52,10 @@ hipError_t launch_gemm_gate_up_mx(const uint16_t* x, const int32_t* row_token,
                                   const int32_t* offsets, int E_loc, int64_t R_cap, int d,
                                   int H, const uint16_t* w_gu, SituCoef c, uint8_t* h_codes,
                                   uint8_t* h_scales, uint16_t* a, hipStream_t s);
+// down: fp32 rows p * o over output columns [c0, c0 + nc): rows_out [R_cap, nc].
 hipError_t launch_gemm_down(const uint16_t* a, const int32_t* offsets, const float* row_gate,
-                            int E_loc, int64_t R_cap, int H, int d, const uint16_t* w_down,
-                            uint16_t* rows_out, hipStream_t s);
+                            int E_loc, int64_t R_cap, int H, int d, int c0, int nc,
+                            const uint16_t* w_down, float* rows_out, hipStream_t s);
 // dA: G = dy[row_token] . w_down[e]; epilogue writes dh, pa = bf16(p a) and dp partials.
 int gemm_da_slots(int H);
 // The saved h is read from bf16 `h`, or from MXFP8 codes and scales when h_codes != nullptr.
@@ -57,10 +64,10 @@ hipError_t launch_gemm_da(const uint16_t* dy, const int32_t* row_token, const in
                           const uint16_t* h, const uint8_t* h_codes, const uint8_t* h_scales,
                           const float* row_gate, SituCoef c, uint16_t* dh, uint16_t* pa,
                           float* dp_part, hipStream_t s);
-// dX rows: dh . w_gu[e]  ->  bf16 rows [R, d]
+// dX rows: dh . w_gu[e] over columns [c0, c0 + nc)  ->  fp32 rows [R_cap, nc]
 hipError_t launch_gemm_dx(const uint16_t* dh, const int32_t* offsets, int E_loc,
-                          int64_t R_cap, int d, int H, const uint16_t* w_gu,
-                          uint16_t* rows_out, hipStream_t s);
+                          int64_t R_cap, int d, int H, int c0, int nc, const uint16_t* w_gu,
+                          float* rows_out, hipStream_t s);
 // Weight gradients with ragged K = rows of the expert.
 hipError_t launch_gemm_dw_down(const uint16_t* dy, const int32_t* row_token,
                                const uint16_t* pa, const int32_t* offsets, int E_loc, int d,
@@ -78,7 +85,7 @@ hipError_t launch_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int
 // W4A8 forward ("Frontier-scale RL with Kimi K3", "Low precision (MXFP4) rollouts"): MXFP8
 // activations x MXFP4 weights on the block-scaled MFMA; K (d for gate_up, H for down) a
 // multiple of 128. gate_up writes a as MXFP8 (codes [R, H], scales [R, H/32]); down writes
-// bf16(p o) rows [R, d].
+// fp32 p o rows [R_cap, nc] for output columns [c0, c0 + nc).
 hipError_t launch_w4a8_gate_up(const uint8_t* x_codes, const uint8_t* x_scales,
                                const int32_t* row_token, const int32_t* offsets, int E_loc,
                                int64_t R_cap, int d, int H, const uint8_t* w_codes,
@@ -86,8 +93,9 @@ hipError_t launch_w4a8_gate_up(const uint8_t* x_codes, const uint8_t* x_scales,
                                uint8_t* a_scales, hipStream_t s);
 hipError_t launch_w4a8_down(const uint8_t* a_codes, const uint8_t* a_scales,
                             const int32_t* offsets, const float* row_gate, int E_loc,
-                            int64_t R_cap, int H, int d, const uint8_t* w_codes,
-                            const uint8_t* w_scales, uint16_t* rows_out, hipStream_t s);
+                            int64_t R_cap, int H, int d, int c0, int nc,
+                            const uint8_t* w_codes, const uint8_t* w_scales, float* rows_out,
+                            hipStream_t s);
 // MXFP4 format of the W4A8 weights (mxfp4.h); n a multiple of 32.
 hipError_t launch_mx4_quantize(const uint16_t* v, int64_t rows, int n, uint8_t* codes,
                                uint8_t* scales, hipStream_t s);

@@ -352,15 +352,19 @@ hipError_t launch_permute(const int32_t* idx, const float* gates, int64_t T, int
 // out[t] = bf16( sum_j w(r) rows[r] ), r = slot_row[t, j] >= 0, in fp32 and slot order.
 // One wavefront per token at a time, so a CU keeps as many tokens in flight as it holds
 // wavefronts. The wave loads the token's k slot entries (and their weights) at once, one per
-// lane, and walks only the local ones, two at a time; each lane owns CPL 16-byte column
-// chunks per pass, so the loads of a pass (2 x CPL per lane) are in flight together. The
-// output row is written with streaming stores.
+// lane, and walks only the local ones, two at a time; each lane owns CPL units of 8
+// consecutive columns per pass (one 16-byte load of bf16 rows, two of fp32 rows), so the
+// loads of a pass are in flight together. The output row is written with streaming stores.
 constexpr int kCombCPL = 4;
-__global__ __launch_bounds__(256) void unpermute_kernel(const uint16_t* __restrict__ rows,
+template <typename RowT>
+__global__ __launch_bounds__(256) void unpermute_kernel(const RowT* __restrict__ rows,
+                                                        int64_t ldr,
                                                         const int32_t* __restrict__ slot_row,
                                                         const float* __restrict__ w,
                                                         int64_t T, int k, int n,
-                                                        uint16_t* __restrict__ out) {
+                                                        uint16_t* __restrict__ out,
+                                                        int64_t ldo) {
+  constexpr int VB = sizeof(RowT) == 2 ? 1 : 2;     // 16-byte loads per 8 columns
   const int nc = n >> 3;
   const int lane = threadIdx.x & 63;
   const int64_t nwave = (int64_t)gridDim.x * (blockDim.x >> 6);
@@ -392,13 +396,17 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const uint16_t* __restri
             nb = b + 1;
           }
         }
-        u32x4 v[2][kCombCPL];
+        u32x4 v[2][kCombCPL][VB];
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
           for (int u = 0; u < kCombCPL; ++u) {
             const int c = c0 + 64 * u + lane;
-            if (b < nb && c < nc) v[b][u] = *(const u32x4*)(rows + (int64_t)rb[b] * n + 8 * c);
+            if (b < nb && c < nc) {
+              const u32x4* src = (const u32x4*)(rows + (int64_t)rb[b] * ldr + 8 * c);
+#pragma unroll
+              for (int vb = 0; vb < VB; ++vb) v[b][u][vb] = src[vb];
+            }
           }
 #pragma unroll
         for (int b = 0; b < 2; ++b)
@@ -406,10 +414,16 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const uint16_t* __restri
           for (int u = 0; u < kCombCPL; ++u) {
             const int c = c0 + 64 * u + lane;
             if (b < nb && c < nc) {
+              if constexpr (VB == 1) {
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                acc[u][2 * q] += wb[b] * bf16_lo(v[b][u][q]);
-                acc[u][2 * q + 1] += wb[b] * bf16_hi(v[b][u][q]);
+                for (int q = 0; q < 4; ++q) {
+                  acc[u][2 * q] += wb[b] * bf16_lo(v[b][u][0][q]);
+                  acc[u][2 * q + 1] += wb[b] * bf16_hi(v[b][u][0][q]);
+                }
+              } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                  acc[u][q] += wb[b] * __uint_as_float(v[b][u][q >> 2][q & 3]);
               }
             }
           }
@@ -421,22 +435,36 @@ __global__ __launch_bounds__(256) void unpermute_kernel(const uint16_t* __restri
           u32x4 o;
 #pragma unroll
           for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[u][2 * q], acc[u][2 * q + 1]);
-          __builtin_nontemporal_store(o, (u32x4*)(out + t * n + 8 * c));
+          __builtin_nontemporal_store(o, (u32x4*)(out + t * ldo + 8 * c));
         }
       }
     }
   }
 }
 
-hipError_t launch_unpermute(const uint16_t* rows, const int32_t* slot_row, const float* w,
-                            int64_t T, int k, int n, uint16_t* out, hipStream_t s) {
+template <typename RowT>
+static hipError_t run_unpermute(const RowT* rows, int64_t ldr, const int32_t* slot_row,
+                                const float* w, int64_t T, int k, int n, uint16_t* out,
+                                int64_t ldo, hipStream_t s) {
   if (T == 0 || n == 0) return hipSuccess;
   int64_t blocks = (T + 3) / 4;
   const int64_t cap = (int64_t)device_cu_count() * 16;
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL(unpermute_kernel, dim3((unsigned)blocks), dim3(256), 0, s, rows,
-                     slot_row, w, T, k, n, out);
+  hipLaunchKernelGGL(unpermute_kernel<RowT>, dim3((unsigned)blocks), dim3(256), 0, s, rows, ldr,
+                     slot_row, w, T, k, n, out, ldo);
   return hipGetLastError();
+}
+
+hipError_t launch_unpermute(const uint16_t* rows, int64_t ldr, const int32_t* slot_row,
+                            const float* w, int64_t T, int k, int n, uint16_t* out,
+                            int64_t ldo, hipStream_t s) {
+  return run_unpermute(rows, ldr, slot_row, w, T, k, n, out, ldo, s);
+}
+
+hipError_t launch_unpermute_f32(const float* rows, int64_t ldr, const int32_t* slot_row,
+                                int64_t T, int k, int n, uint16_t* out, int64_t ldo,
+                                hipStream_t s) {
+  return run_unpermute(rows, ldr, slot_row, (const float*)nullptr, T, k, n, out, ldo, s);
 }
 
 // ------------------------------------------------------------------------------ dp

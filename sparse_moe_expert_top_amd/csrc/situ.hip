@@ -15,6 +15,7 @@
 // (KU = 4) and 6.0 TB/s backward (KU = 2), against 5.4-5.6 TB/s for a grid-stride walk of
 // 256 workgroups per CU; plain (temporal) loads cost 5-10 %.
 #include <hip/hip_runtime.h>
+#include <stdlib.h>
 
 #include "common.h"
 #include "launch.h"
@@ -122,9 +123,15 @@ __global__ __launch_bounds__(256) void situ_bwd_kernel(const uint16_t* __restric
 }
 
 // Rows per launch: each launch covers fewer than 2^32 chunks (H / 8 per row), with room for
-// the last block's overhang.
+// the last block's overhang. MOE_SITU_ROWS_PER_LAUNCH (environment, read per call) may lower
+// it, so the split across launches can be exercised on small inputs.
 static int64_t situ_rows_per_launch(int H) {
-  return (((int64_t)1 << 32) - 4096) / (H / 8);
+  int64_t step = (((int64_t)1 << 32) - 4096) / (H / 8);
+  if (const char* env = getenv("MOE_SITU_ROWS_PER_LAUNCH")) {
+    const long long v = atoll(env);
+    if (v > 0 && v < step) step = v;
+  }
+  return step;
 }
 
 hipError_t launch_situ_fwd(const uint16_t* h, int64_t R, int H, SituCoef c, uint16_t* a,

@@ -19,7 +19,8 @@ with the weights quantized once to MXFP4 (`W4A8Weights`).
 
 `LayerBuffers` allocates every buffer once (torch, HBM) so a training step issues only the
 library's kernels; buffers indexed by routed rows are sized by a capacity R_cap (T*k by
-default, which never overflows).
+default, which never overflows, or the exact routed rows of given logits), and the forward's
+transients share their memory with the backward workspace.
 """
 from __future__ import annotations
 
@@ -59,44 +60,76 @@ class W4A8Weights:
         self.down_scales = ds.view(E_loc, d, H // 32)
 
 
+def _round256(n: int) -> int:
+    return (int(n) + 255) // 256 * 256
+
+
 class LayerBuffers:
-    """Device buffers for one layer call of a given shape, reused across steps."""
+    """Device buffers for one layer call of a given shape, reused across steps.
+
+    Row-indexed buffers are sized by the row capacity R_cap: T*k by default (never overflows),
+    or the exact routed-row count of given logits (`routed_rows`). With alias=True the
+    forward's transients (a and the down combine's fp32 rows) and the backward workspace share
+    one arena: the forward's transients are dead once y is written, so the layer holds the
+    saved h plus the larger of the two. combine_passes > 1 runs each combine in that many
+    passes over the output columns, shrinking the fp32 row buffers by that factor at the cost
+    of re-reading the GEMM's row operand once per pass (results are bit-identical)."""
 
     def __init__(self, shape: LayerShape, R_cap: int | None = None, device="cuda",
-                 h_store: str = "bf16"):
+                 h_store: str = "bf16", alias: bool = True, combine_passes: int = 1):
         if h_store not in ("bf16", "mxfp8"):
             raise ValueError(f"h_store must be 'bf16' or 'mxfp8', not {h_store!r}")
         s = shape
         self.shape = s
         self.h_store = h_store
         self.R_cap = s.T * s.k if R_cap is None else int(R_cap)
+        self.combine_passes = int(combine_passes)
         R = max(self.R_cap, 1)
-        i32, f32, bf = torch.int32, torch.float32, torch.bfloat16
+        i32, f32, bf, u8 = torch.int32, torch.float32, torch.bfloat16, torch.uint8
         e = lambda *sh, dt: torch.empty(sh, dtype=dt, device=device)
         self.topk_idx = e(s.T, s.k, dt=i32)
         self.gates = e(s.T, s.k, dt=f32)
         self.perm = dict(offsets=e(s.E_loc + 1, dt=i32), row_token=e(R, dt=i32),
                          row_gate=e(R, dt=f32), slot_row=e(s.T, s.k, dt=i32),
                          status=e(1, dt=i32))
-        self.ws_perm = e(max(_lib.workspace_size(_lib.MOE_WS_PERMUTE, T=s.T, E_loc=s.E_loc), 256), dt=torch.uint8)
+        self.ws_perm = e(max(_lib.workspace_size(_lib.MOE_WS_PERMUTE, T=s.T, E_loc=s.E_loc), 256), dt=u8)
         if h_store == "mxfp8":
             self.h = None
-            self.h_codes = e(R, 2 * s.H, dt=torch.uint8)
-            self.h_scales = e(R, 2 * s.H // 32, dt=torch.uint8)
+            self.h_codes = e(R, 2 * s.H, dt=u8)
+            self.h_scales = e(R, 2 * s.H // 32, dt=u8)
         else:
             self.h = e(R, 2 * s.H, dt=bf)
-        self.a = e(R, s.H, dt=bf)
+        sizes = dict(T=s.T, E_loc=s.E_loc, k=s.k, d=s.d, H=s.H, R_cap=self.R_cap)
+        down_b = max(_lib.workspace_size_passes(_lib.MOE_WS_DOWN_COMBINE, self.combine_passes,
+                                                **sizes), 256)
+        bwd_b = max(_lib.workspace_size_passes(_lib.MOE_WS_EXPERT_BWD, self.combine_passes,
+                                               **sizes), 256)
+        a_b = _round256(R * s.H * 2)
+        if alias:
+            self.arena = e(max(a_b + down_b, bwd_b), dt=u8)
+            self.a = self.arena[:R * s.H * 2].view(bf).view(R, s.H)
+            self.ws_down = self.arena[a_b:a_b + down_b]
+            self.ws_bwd = self.arena[:bwd_b]
+        else:
+            self.arena = None
+            self.a = e(R, s.H, dt=bf)
+            self.ws_down = e(down_b, dt=u8)
+            self.ws_bwd = e(bwd_b, dt=u8)
         self.y = e(s.T, s.d, dt=bf)
-        self.ws_down = e(max(_lib.workspace_size(_lib.MOE_WS_DOWN_COMBINE, T=s.T, E_loc=s.E_loc,
-                                                 k=s.k, d=s.d, H=s.H, R_cap=self.R_cap), 256),
-                         dt=torch.uint8)
         self.dx = e(s.T, s.d, dt=bf)
         self.dw_gu = e(s.E_loc, 2 * s.H, s.d, dt=f32)
         self.dw_down = e(s.E_loc, s.d, s.H, dt=f32)
         self.dp = e(s.T, s.k, dt=f32)
-        self.ws_bwd = e(max(_lib.workspace_size(_lib.MOE_WS_EXPERT_BWD, T=s.T, E_loc=s.E_loc,
-                                                k=s.k, d=s.d, H=s.H, R_cap=self.R_cap), 256),
-                        dt=torch.uint8)
+
+    @staticmethod
+    def routed_rows(shape: LayerShape, logits, device="cuda") -> int:
+        """Local routed rows R of these logits (routes and permutes once with capacity T*k;
+        reads 4 bytes back, so it synchronises). Sizing buffers at R_cap = R fits these logits
+        exactly; other logits may route more rows (moe_permute then clamps and flags)."""
+        s = shape
+        idx, gates = _lib.moe_route_topk(logits, s.k)
+        perm = _lib.moe_permute(idx, gates, s.e_lo, s.E_loc, s.T * s.k)
+        return int(perm["offsets"][-1].item())
 
     # ------------------------------------------------------------------ steps
     def route(self, logits):
@@ -105,9 +138,9 @@ class LayerBuffers:
         _lib.moe_permute(self.topk_idx, self.gates, s.e_lo, s.E_loc, self.R_cap, out=self.perm,
                          ws=self.ws_perm)
 
-    def forward(self, x, logits, w_gu, w_down):
+    def gate_up(self, x, w_gu):
+        """Gate/up GEMM with the SiTU-GLU epilogue: the saved h (bf16 or MXFP8) and a."""
         s = self.shape
-        self.route(logits)
         if self.h_store == "mxfp8":
             _lib.moe_grouped_gemm_gate_up_mx(x, self.perm["row_token"], self.perm["offsets"],
                                              w_gu, self.R_cap, s.beta, s.linear_beta,
@@ -116,10 +149,18 @@ class LayerBuffers:
         else:
             _lib.moe_grouped_gemm_gate_up(x, self.perm["row_token"], self.perm["offsets"], w_gu,
                                           self.R_cap, s.beta, s.linear_beta, h=self.h, a=self.a)
+
+    def down_combine(self, w_down):
+        """Down GEMM and combine into y."""
         _lib.moe_grouped_gemm_down_combine(self.a, self.perm["offsets"], self.perm["row_gate"],
                                            self.perm["slot_row"], w_down, self.R_cap, y=self.y,
                                            ws=self.ws_down)
         return self.y
+
+    def forward(self, x, logits, w_gu, w_down):
+        self.route(logits)
+        self.gate_up(x, w_gu)
+        return self.down_combine(w_down)
 
     def forward_w4a8(self, x, logits, w4: W4A8Weights):
         """W4A8 forward: x quantized to MXFP8 per token, a to MXFP8 per row; y in bf16."""
@@ -143,17 +184,15 @@ class LayerBuffers:
                                                 y=self.y, ws=self.ws_down)
         return self.y
 
-    def backward(self, dy, x, w_gu, w_down):
+    def backward(self, dy, x, w_gu, w_down, stages=_lib.MOE_BWD_ALL):
+        """The backward, or the subset of its stages in `stages` (MOE_BWD_* bits; calls over
+        one backward run the stages in their fixed order)."""
         s = self.shape
-        if self.h_store == "mxfp8":
-            _lib.moe_expert_bwd_mx(dy, x, self.h_codes, self.h_scales, self.perm, w_gu, w_down,
-                                   self.R_cap, s.beta, s.linear_beta, dx=self.dx,
-                                   dw_gu=self.dw_gu, dw_down=self.dw_down, dp=self.dp,
-                                   ws=self.ws_bwd)
-        else:
-            _lib.moe_expert_bwd(dy, x, self.h, self.perm, w_gu, w_down, self.R_cap, s.beta,
-                                s.linear_beta, dx=self.dx, dw_gu=self.dw_gu,
-                                dw_down=self.dw_down, dp=self.dp, ws=self.ws_bwd)
+        hk = (dict(h_codes=self.h_codes, h_scales=self.h_scales) if self.h_store == "mxfp8"
+              else dict(h=self.h))
+        _lib.moe_expert_bwd_stages(dy, x, self.perm, w_gu, w_down, self.R_cap, stages, self.dx,
+                                   self.dw_gu, self.dw_down, self.dp, self.ws_bwd,
+                                   beta=s.beta, linear_beta=s.linear_beta, **hk)
         return self.dx, self.dw_gu, self.dw_down, self.dp
 
     def step(self, x, logits, w_gu, w_down, dy):

@@ -46,16 +46,70 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def run_layer(m, cfg, inp, R_cap=None, h_store="bf16"):
-    """Forward + backward through LayerBuffers (the benchmark's launch configuration)."""
-    shape = m.LayerShape(T=inp["x"].shape[0], E=cfg.E, k=cfg.k, e_lo=cfg.e_lo, E_loc=cfg.E_loc,
-                         d=cfg.d, H=cfg.H, beta=cfg.beta, linear_beta=cfg.linear_beta)
-    buf = m.LayerBuffers(shape, R_cap=R_cap, h_store=h_store)
+def layer_shape(m, cfg, T=None):
+    return m.LayerShape(T=cfg.T if T is None else T, E=cfg.E, k=cfg.k, e_lo=cfg.e_lo,
+                        E_loc=cfg.E_loc, d=cfg.d, H=cfg.H, beta=cfg.beta,
+                        linear_beta=cfg.linear_beta)
+
+
+def run_layer(m, cfg, inp, R_cap=None, h_store="bf16", **buf_kw):
+    """Forward + backward through LayerBuffers (the benchmark's launch configuration). The
+    forward's activation `a` shares memory with the backward workspace, so a copy taken after
+    the forward is kept as buf.a_fwd."""
+    buf = m.LayerBuffers(layer_shape(m, cfg, inp["x"].shape[0]), R_cap=R_cap, h_store=h_store,
+                         **buf_kw)
     t = dict(x=dev_bf16(inp["x"]), logits=dev(inp["logits"]), w_gu=dev_bf16(inp["w_gu"]),
              w_down=dev_bf16(inp["w_down"]), dy=dev_bf16(inp["dy"]))
-    buf.step(t["x"], t["logits"], t["w_gu"], t["w_down"], t["dy"])
+    buf.forward(t["x"], t["logits"], t["w_gu"], t["w_down"])
+    buf.a_fwd = buf.a.clone()
+    if buf.combine_passes == 1:
+        buf.rows_fwd = rows_f32(buf, cfg.d)
+    buf.backward(t["dy"], t["x"], t["w_gu"], t["w_down"])
     torch.cuda.synchronize()
     return buf, t
+
+
+def bf16_half_step(v):
+    """Half the spacing of the bf16 grid at |v| (8 significant bits; 2^-134 below 2^-126)."""
+    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -126)))
+    return np.ldexp(1.0, (e - 8).astype(np.int64))
+
+
+def rows_f32(buf, n):
+    """The fp32 rows the down GEMM left in the combine's workspace (one pass: [R_cap, n])."""
+    R = buf.R_cap
+    return buf.ws_down[: R * n * 4].view(torch.float32).view(R, n).cpu().numpy().astype(np.float64)
+
+
+def check_rounded_once(y, rows, slot_row, what):
+    """The combine rounds each output once: y[t] is the bf16 rounding (nearest, ties to even)
+    of the fp32 sum of the token's fp32 rows in slot order. The exact sum S of those rows (fp64
+    here) and the fp32 sum differ by at most (k - 1) 2^-24 sum|rows|, so y must lie within half
+    a bf16 step of S plus that; rows rounded to bf16 before the sum would miss it by up to k
+    half steps of the terms. Also checks that the rows are not bf16 values themselves."""
+    T, k = slot_row.shape
+    S = np.zeros_like(y)
+    M = np.zeros_like(y)
+    for j in range(k):
+        r = slot_row[:, j]
+        m = r >= 0
+        S[m] += rows[r[m]]
+        M[m] += np.abs(rows[r[m]])
+    bound = bf16_half_step(S) + (k - 1) * 2.0 ** -24 * M + 2.0 ** -149
+    err = np.abs(y - S)
+    bad = err > bound
+    assert not bad.any(), (what, int(bad.sum()), np.argwhere(bad)[:3])
+    used = np.unique(slot_row[slot_row >= 0])
+    if len(used):
+        low = rows[used].astype(np.float32).view(np.uint32) & 0xFFFF
+        assert np.mean(low != 0) > 0.9, (what, "rows look bf16-rounded")
+
+
+def rel_to_sum(got, exact):
+    """max|got - exact| / max|exact|: against the oracle's fp64 sum before its final rounding
+    (reported; half a bf16 step at the top of the range is 2^-8 = 3.9e-3 of the maximum)."""
+    m = float(np.max(np.abs(exact))) if exact.size else 0.0
+    return 0.0 if m == 0.0 else float(np.max(np.abs(np.asarray(got, np.float64) - exact)) / m)
 
 
 def check_route_perm(buf, idx, gates, perm, R_cap=None):
@@ -75,15 +129,24 @@ def check_route_perm(buf, idx, gates, perm, R_cap=None):
 
 
 # ------------------------------------------------------------------------------- SiTU-GLU
-@pytest.mark.parametrize("R,H", [(1000, 192), (37, 64), (1, 8)])
-def test_situ_glu_small(moe, R, H):
-    say(f"situ_glu R={R} H={H}")
+@pytest.mark.parametrize("R,H,rows_per_launch", [(1000, 192, 0), (37, 64, 0), (1, 8, 0),
+                                                 (1000, 192, 300), (1000, 192, 1)])
+def test_situ_glu_small(moe, R, H, rows_per_launch):
+    """rows_per_launch > 0 caps the rows of one launch (MOE_SITU_ROWS_PER_LAUNCH), so the
+    split across launches that very large inputs take (below 2^32 chunks each) is exercised:
+    4 launches of 300, 300, 300 and 100 rows, or one launch per row."""
+    say(f"situ_glu R={R} H={H} rows_per_launch={rows_per_launch}")
     inp = situ_inputs(R, H, seed=3)
     h = dev_bf16(inp["h"])
     da = dev_bf16(inp["da"])
-    a = moe.situ_glu_fwd(h)
-    dh = moe.situ_glu_bwd(h, da)
-    torch.cuda.synchronize()
+    if rows_per_launch:
+        os.environ["MOE_SITU_ROWS_PER_LAUNCH"] = str(rows_per_launch)
+    try:
+        a = moe.situ_glu_fwd(h)
+        dh = moe.situ_glu_bwd(h, da)
+        torch.cuda.synchronize()
+    finally:
+        os.environ.pop("MOE_SITU_ROWS_PER_LAUNCH", None)
     hf = oracle.bf16_widen(inp["h"])
     ref_a = oracle.bf16_round(oracle.situ_glu_fwd(hf, H))
     ref_dh = oracle.bf16_round(oracle.situ_glu_bwd(hf, oracle.bf16_widen(inp["da"]), H))
@@ -248,9 +311,13 @@ def test_router_bwd(moe):
 
 # ------------------------------------------------------------------------------- layer, full compare
 MID = LayerConfig("mid", T=2048, d=256, H=192, E=16, k=4, e_lo=2, E_loc=10)
+# every GEMM spans two or more N tiles (gate/up 5 pair tiles, down and dX 3, dA 3 with a
+# half tile, dW_down 3 x 3, dW_gu 5 x 3) and the zipf bias makes the experts' rows uneven
+MULTI = LayerConfig("multi_tile", T=1536, d=768, H=640, E=8, k=2, e_lo=0, E_loc=8, bias="zipf")
 SMALL_CASES = {
     "tiny": LAYER_CONFIGS["tiny"],
     "mid": MID,                                                           # several tiles + ragged tails
+    "multi_tile": MULTI,
     "one_token": LayerConfig("one_token", T=1, d=128, H=64, E=8, k=3, e_lo=0, E_loc=8),
     "k_eq_E": LayerConfig("k_eq_E", T=64, d=64, H=128, E=6, k=6, e_lo=0, E_loc=6),
     "none_local": LayerConfig("none_local", T=128, d=128, H=64, E=64, k=2, e_lo=60, E_loc=4),
@@ -259,25 +326,30 @@ SMALL_CASES = {
 }
 
 
-def compare_full(m, cfg, inp, R_cap=None):
+def compare_full(m, cfg, inp, R_cap=None, **buf_kw):
     idx, gates, perm = oracle_route_perm(inp, cfg)
-    buf, t = run_layer(m, cfg, inp, R_cap)
+    buf, t = run_layer(m, cfg, inp, R_cap, **buf_kw)
     check_route_perm(buf, idx, gates, perm)
     f = oracle.expert_layer_fwd(inp["x"], inp["w_gu"], inp["w_down"], perm, cfg.H, mode="S")
     b = oracle.expert_layer_bwd(inp["x"], inp["dy"], inp["w_gu"], inp["w_down"], perm, cfg.H,
                                 mode="S")
     R = perm["R"]
+    gy, gdx = host_bf16(buf.y), host_bf16(buf.dx)
     errs = dict(
         h=rel_err(host_bf16(buf.h[:R]), f["h"]) if R else 0.0,
-        y=rel_err(host_bf16(buf.y), f["y"]),
-        dx=rel_err(host_bf16(buf.dx), b["dx"]),
+        y=rel_err(gy, f["y"]),
+        dx=rel_err(gdx, b["dx"]),
         dw_gu=rel_err(buf.dw_gu.cpu().numpy(), b["dw_gu"]),
         dw_down=rel_err(buf.dw_down.cpu().numpy(), b["dw_down"]),
         dp=rel_err(buf.dp.cpu().numpy(), b["dp"]),
     )
     if R:
-        errs["a"] = rel_err(host_bf16(buf.a[:R]), f["a"])
-    say(cfg.name, "R", R, {k: f"{v:.2e}" for k, v in errs.items()})
+        errs["a"] = rel_err(host_bf16(buf.a_fwd[:R]), f["a"])
+    if buf.combine_passes == 1:
+        check_rounded_once(gy, buf.rows_fwd, perm["slot_row"], f"{cfg.name} y")
+    once = dict(y=rel_to_sum(gy, f["y_sum"]), dx=rel_to_sum(gdx, b["dx_sum"]))
+    say(cfg.name, "R", R, {k: f"{v:.2e}" for k, v in errs.items()},
+        "vs pre-rounding sums:", {k: f"{v:.2e}" for k, v in once.items()})
     for k_, v in errs.items():
         assert v <= (FP32_TOL if k_ == "dp" else BF16_TOL), (k_, v)
     return buf, t, perm
@@ -298,10 +370,37 @@ def test_layer_full(moe, name):
 
 
 def test_layer_exact_capacity(moe):
-    """R_cap equal to the routed rows (the tightest legal buffers)."""
+    """R_cap equal to the routed rows (the tightest legal buffers), found on the device."""
     inp = layer_inputs(MID, seed=1)
     _, _, perm = oracle_route_perm(inp, MID)
-    compare_full(moe, MID, inp, R_cap=perm["R"])
+    R = moe.LayerBuffers.routed_rows(layer_shape(moe, MID), dev(inp["logits"]))
+    assert R == perm["R"]
+    compare_full(moe, MID, inp, R_cap=R)
+
+
+def test_layer_combine_passes_bit_identical(moe):
+    """The combines in 1, 2 or 3 passes over the output columns (d = 768: windows of 768, 512
+    + 256, 256) and with or without the forward/backward memory overlay give bit-identical
+    results; the one-pass run is also compared with the oracle."""
+    inp = layer_inputs(MULTI, seed=6)
+    _, _, perm = oracle_route_perm(inp, MULTI)
+    ref, _, _ = compare_full(moe, MULTI, inp, R_cap=perm["R"], alias=False)
+    for passes, alias in ((2, True), (3, True), (3, False)):
+        say(f"combine passes {passes} alias {alias}")
+        buf, _ = run_layer(moe, MULTI, inp, R_cap=perm["R"], alias=alias, combine_passes=passes)
+        for name in ("y", "dx", "dw_gu", "dw_down", "dp", "h"):
+            assert torch.equal(getattr(buf, name), getattr(ref, name)), (passes, alias, name)
+        assert torch.equal(buf.a_fwd, ref.a_fwd)
+    # the backward in separate stage calls (as the benchmark times it) is the same backward
+    buf, t = run_layer(moe, MULTI, inp, R_cap=perm["R"])
+    for name in ("dx", "dw_gu", "dw_down", "dp"):
+        getattr(buf, name).zero_()
+    for st in (moe.MOE_BWD_DA, moe.MOE_BWD_DW_DOWN, moe.MOE_BWD_DW_GU,
+               moe.MOE_BWD_DX | moe.MOE_BWD_DP):
+        buf.backward(t["dy"], t["x"], t["w_gu"], t["w_down"], stages=st)
+    torch.cuda.synchronize()
+    for name in ("dx", "dw_gu", "dw_down", "dp"):
+        assert torch.equal(getattr(buf, name), getattr(ref, name)), ("stages", name)
 
 
 def test_layer_deterministic_and_recompute_exact(moe):
@@ -312,7 +411,7 @@ def test_layer_deterministic_and_recompute_exact(moe):
     R = buf.rows()
     y1, dx1 = buf.y.clone(), buf.dx.clone()
     dwg1, dwd1, dp1 = buf.dw_gu.clone(), buf.dw_down.clone(), buf.dp.clone()
-    a1 = buf.a[:R].clone()
+    a1 = buf.a_fwd[:R].clone()
     buf.step(t["x"], t["logits"], t["w_gu"], t["w_down"], t["dy"])
     torch.cuda.synchronize()
     for u, v in ((y1, buf.y), (dx1, buf.dx), (dwg1, buf.dw_gu), (dwd1, buf.dw_down), (dp1, buf.dp)):
@@ -345,17 +444,37 @@ def test_layer_token_permutation(moe):
 
 
 # ------------------------------------------------------------------------------- layer, full-size sampled
+def check_h_codes(got_c, got_s, h_ref, what):
+    """The saved h as MXFP8 (codes, scale bytes) against the oracle's MXFP8 of its own bf16 h.
+    The GPU's bf16 h can sit one bf16 step from the oracle's where its fp32 sum lies next to a
+    rounding boundary; that moves an E4M3 code by one step at most or, when a block's largest
+    magnitude crosses a power of two, its scale byte by one (the block's largest value may
+    then move by two steps of the finer grid, its saturation band). Bound per element: two
+    E4M3 steps at the larger of the two scales plus one bf16 step of h. Nearly all codes and
+    scale bytes must be identical."""
+    ref_c, ref_s = oracle.mxfp8.quantize(h_ref)
+    g = oracle.mxfp8.dequantize(got_c, got_s)
+    r = oracle.mxfp8.dequantize(ref_c, ref_s)
+    X = np.maximum(got_s, ref_s).astype(np.int64).repeat(32, axis=1) - 127
+    tol = 2.0 * e4m3_step(r, X) + 2.0 ** -7 * np.abs(h_ref)
+    diff = np.abs(g - r)
+    same_c = float(np.mean(got_c == ref_c))
+    same_s = float(np.mean(got_s == ref_s))
+    say(what, f"h codes identical {same_c:.5f}, scale bytes identical {same_s:.5f}, worst "
+        f"|dh|/tol {float(np.max(diff / tol)):.3f}")
+    assert not (diff > tol).any(), (what, np.argwhere(diff > tol)[:5])
+    assert np.all(np.abs(got_s.astype(np.int64) - ref_s.astype(np.int64)) <= 1), what
+    assert same_c >= 0.999 and same_s >= 0.999, (what, same_c, same_s)
+
+
 def compare_sampled(m, cfg, n_tok=48, n_exp=3, n_col=6, seed=0, h_store="bf16"):
-    """Sampled comparison at full size. h_store="mxfp8" runs the MXFP8-store path on dyadic
-    inputs (h exact on both sides), checks the stored codes and scales of the sampled rows bit
-    for bit and takes weight-gradient columns in whole 32-column blocks."""
+    """Sampled comparison at full size: tokens (all their local rows), their rows' h and a,
+    and the weight-gradient columns of sampled experts (incl. empty ones). h_store="mxfp8"
+    runs the MXFP8-store path; its stored codes are checked within a bound and its weight-
+    gradient columns are taken in whole 32-column blocks (a block shares one scale)."""
     mx = h_store == "mxfp8"
     say(f"layer sampled {cfg.name} ({h_store}): generating inputs")
-    if mx:
-        from moe_inputs import dyadic_layer_inputs
-        inp = dyadic_layer_inputs(cfg, seed=0)
-    else:
-        inp = layer_inputs(cfg, seed=0)
+    inp = layer_inputs(cfg, seed=0)
     say(f"layer sampled {cfg.name}: oracle routing")
     idx, gates, perm = oracle_route_perm(inp, cfg)
     say(f"layer sampled {cfg.name}: GPU step (R={perm['R']})")
@@ -373,18 +492,20 @@ def compare_sampled(m, cfg, n_tok=48, n_exp=3, n_col=6, seed=0, h_store="bf16"):
     toks = np.unique(toks)
     tt = torch.from_numpy(toks).cuda()
     rr = torch.from_numpy(rows).cuda()
+    gy, gdx = host_bf16(buf.y[tt]), host_bf16(buf.dx[tt])
     errs = dict(
-        y=rel_err(host_bf16(buf.y[tt]), f["y"][toks]),
-        dx=rel_err(host_bf16(buf.dx[tt]), b["dx"][toks]),
+        y=rel_err(gy, f["y"][toks]),
+        dx=rel_err(gdx, b["dx"][toks]),
         dp=rel_err(buf.dp[tt].cpu().numpy(), b["dp"][toks]),
-        a=rel_err(host_bf16(buf.a[rr]), f["a"]),
+        a=rel_err(host_bf16(buf.a_fwd[rr]), f["a"]),
     )
+    once = dict(y=rel_to_sum(gy, f["y_sum"][toks]))
     if mx:
-        ref_c, ref_s = oracle.mxfp8.quantize(f["h"])
-        assert np.array_equal(buf.h_codes[rr].cpu().numpy(), ref_c)
-        assert np.array_equal(buf.h_scales[rr].cpu().numpy(), ref_s)
+        check_h_codes(buf.h_codes[rr].cpu().numpy(), buf.h_scales[rr].cpu().numpy(), f["h"],
+                      f"{cfg.name} sampled")
     else:
         errs["h"] = rel_err(host_bf16(buf.h[rr]), f["h"])
+        once["dx"] = rel_to_sum(gdx, b["dx_sum"][toks])
     # weight gradients: sampled experts x intermediate columns (all rows of the expert)
     counts = np.diff(perm["offsets"])
     exps = list(rng.choice(cfg.E_loc, n_exp, replace=False))
@@ -398,7 +519,6 @@ def compare_sampled(m, cfg, n_tok=48, n_exp=3, n_col=6, seed=0, h_store="bf16"):
         cols = np.unique(np.concatenate([rng.choice(cfg.H, n_col, replace=False), [0, cfg.H - 1]]))
     dwg = buf.dw_gu
     dwd = buf.dw_down
-    e_gu, e_dn = [], []
     ref_gu_all, ref_dn_all, got_gu_all, got_dn_all = [], [], [], []
     for e in exps:
         say(f"layer sampled {cfg.name}: dW expert {e} rows {counts[e]}")
@@ -411,7 +531,8 @@ def compare_sampled(m, cfg, n_tok=48, n_exp=3, n_col=6, seed=0, h_store="bf16"):
         ref_dn_all.append(dn)
     errs["dw_gu"] = rel_err(np.stack(got_gu_all), np.stack(ref_gu_all))
     errs["dw_down"] = rel_err(np.stack(got_dn_all), np.stack(ref_dn_all))
-    say(cfg.name, "R", perm["R"], {k: f"{v:.2e}" for k, v in errs.items()})
+    say(cfg.name, "R", perm["R"], {k: f"{v:.2e}" for k, v in errs.items()},
+        "vs pre-rounding sums:", {k: f"{v:.2e}" for k, v in once.items()})
     for k_, v in errs.items():
         assert v <= (FP32_TOL if k_ == "dp" else BF16_TOL), (k_, v)
     # properties over the whole tensors
@@ -433,9 +554,42 @@ def test_layer_full_size_sampled(moe, name):
 
 
 def test_layer_mxfp8_full_size_sampled(moe):
-    """The MXFP8-store path at the shard workload's full size."""
+    """The MXFP8-store path at the shard workload's full size, on the workload's own inputs."""
     compare_sampled(moe, LAYER_CONFIGS["shard"], h_store="mxfp8")
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ router backward, end to end
+ROUTER_CASES = {
+    "tiny": LAYER_CONFIGS["tiny"],
+    # the large-context workload's shapes (16 of 28 local experts, every route local) at 512
+    # tokens, so the oracle runs the whole layer
+    "large_512": LayerConfig("large_512", T=512, d=3584, H=3072, E=28, k=16, e_lo=0, E_loc=28),
+}
+
+
+@pytest.mark.parametrize("name", list(ROUTER_CASES))
+def test_router_bwd_end_to_end(moe, name):
+    """dp from the layer's backward feeds the router backward: dlogits against the oracle's
+    router_bwd of its own gates and dp (every route is local, so dp is complete)."""
+    cfg = ROUTER_CASES[name]
+    say(f"router bwd end to end {name}")
+    inp = layer_inputs(cfg, seed=0)
+    idx, gates, perm = oracle_route_perm(inp, cfg)
+    assert perm["R"] == cfg.T * cfg.k
+    buf, t = run_layer(moe, cfg, inp)
+    check_route_perm(buf, idx, gates, perm)
+    dl = moe.moe_router_bwd(buf.gates, buf.dp)
+    torch.cuda.synchronize()
+    say(f"router bwd end to end {name}: oracle")
+    b = oracle.expert_layer_bwd(inp["x"], inp["dy"], inp["w_gu"], inp["w_down"], perm, cfg.H,
+                                mode="S")
+    ref = oracle.router_bwd(gates, b["dp"])
+    errs = dict(dp=rel_err(buf.dp.cpu().numpy(), b["dp"]), dlogits=rel_err(dl.cpu().numpy(), ref))
+    say(name, {k: f"{v:.2e}" for k, v in errs.items()})
+    assert errs["dp"] <= FP32_TOL and errs["dlogits"] <= FP32_TOL
+    # softmax gradient: each token's dlogits sum to zero
+    assert float(dl.double().sum(1).abs().max()) <= 1e-5 * float(dl.abs().max())
 
 
 # ------------------------------------------------------------------ MXFP8 storage of the saved h
@@ -481,7 +635,9 @@ def test_layer_mxfp8_store(moe, name):
     t = dict(x=dev_bf16(inp["x"]), logits=dev(inp["logits"]), w_gu=dev_bf16(inp["w_gu"]),
              w_down=dev_bf16(inp["w_down"]), dy=dev_bf16(inp["dy"]))
     buf = moe.LayerBuffers(shape, h_store="mxfp8")
-    buf.step(t["x"], t["logits"], t["w_gu"], t["w_down"], t["dy"])
+    buf.forward(t["x"], t["logits"], t["w_gu"], t["w_down"])
+    a_mx = buf.a.clone()
+    buf.backward(t["dy"], t["x"], t["w_gu"], t["w_down"])
     ref16 = moe.LayerBuffers(shape)
     ref16.forward(t["x"], t["logits"], t["w_gu"], t["w_down"])
     torch.cuda.synchronize()
@@ -492,7 +648,7 @@ def test_layer_mxfp8_store(moe, name):
     ref_c, ref_s = oracle.mxfp8.quantize(f["h"])
     assert np.array_equal(buf.h_codes[:R].cpu().numpy(), ref_c)
     assert np.array_equal(buf.h_scales[:R].cpu().numpy(), ref_s)
-    assert torch.equal(buf.a[:R].view(torch.int16), ref16.a[:R].view(torch.int16))
+    assert torch.equal(a_mx[:R].view(torch.int16), ref16.a[:R].view(torch.int16))
     assert torch.equal(buf.y.view(torch.int16), ref16.y.view(torch.int16))
     b = oracle.expert_layer_bwd(inp["x"], inp["dy"], inp["w_gu"], inp["w_down"], perm, cfg.H,
                                 mode="S", h_store="mxfp8")
@@ -507,6 +663,34 @@ def test_layer_mxfp8_store(moe, name):
     b16 = oracle.expert_layer_bwd(inp["x"], inp["dy"], inp["w_gu"], inp["w_down"], perm, cfg.H,
                                   mode="S")
     assert rel_err(b16["dp"], b["dp"]) > FP32_TOL
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "multi_tile"])
+def test_layer_mxfp8_store_general(moe, name):
+    """The MXFP8-store layer on the workloads' own inputs (x ~ N(0,1), weights N(0, 1/fan_in)):
+    the stored codes within the bound of check_h_codes; y, a and h's forward as in the
+    bf16-store path; dx, dW and dp against the oracle recomputing from its own stored h."""
+    cfg = SMALL_CASES[name]
+    say(f"layer mxfp8 general {name}")
+    inp = layer_inputs(cfg, seed=0)
+    idx, gates, perm = oracle_route_perm(inp, cfg)
+    buf, t = run_layer(moe, cfg, inp, h_store="mxfp8")
+    check_route_perm(buf, idx, gates, perm)
+    ref16, _ = run_layer(moe, cfg, inp)
+    R = perm["R"]
+    f = oracle.expert_layer_fwd(inp["x"], inp["w_gu"], inp["w_down"], perm, cfg.H, mode="S")
+    check_h_codes(buf.h_codes[:R].cpu().numpy(), buf.h_scales[:R].cpu().numpy(), f["h"], name)
+    assert torch.equal(buf.a_fwd[:R].view(torch.int16), ref16.a_fwd[:R].view(torch.int16))
+    assert torch.equal(buf.y.view(torch.int16), ref16.y.view(torch.int16))
+    b = oracle.expert_layer_bwd(inp["x"], inp["dy"], inp["w_gu"], inp["w_down"], perm, cfg.H,
+                                mode="S", h_store="mxfp8")
+    errs = dict(dx=rel_err(host_bf16(buf.dx), b["dx"]),
+                dw_gu=rel_err(buf.dw_gu.cpu().numpy(), b["dw_gu"]),
+                dw_down=rel_err(buf.dw_down.cpu().numpy(), b["dw_down"]),
+                dp=rel_err(buf.dp.cpu().numpy(), b["dp"]))
+    say(name, "R", R, {k: f"{v:.2e}" for k, v in errs.items()})
+    for k_, v in errs.items():
+        assert v <= (FP32_TOL if k_ == "dp" else BF16_TOL), (k_, v)
 
 
 # ------------------------------------------------------------------ W4A8 forward (MXFP4 weights)
@@ -616,8 +800,11 @@ def compare_w4a8_full(m, cfg, inp, R_cap=None):
     R = perm["R"]
     check_a_codes(buf.a_codes[:R].cpu().numpy(), buf.a_scales[:R].cpu().numpy(), f,
                   np.arange(R), cfg.H, cfg.beta, cfg.name)
-    err = rel_err(host_bf16(buf.y), f["y"])
-    say(cfg.name, "R", R, f"y {err:.2e}")
+    gy = host_bf16(buf.y)
+    err = rel_err(gy, f["y"])
+    check_rounded_once(gy, rows_f32(buf, cfg.d), perm["slot_row"], f"{cfg.name} y")
+    once = rel_to_sum(gy, f["y_sum"])
+    say(cfg.name, "R", R, f"y {err:.2e}, vs pre-rounding sum {once:.2e}")
     assert err <= BF16_TOL
     return buf, perm
 
