@@ -194,6 +194,29 @@ moe_status moe_grouped_gemm_down_combine(const void* a, const int32_t* expert_of
                                          void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * moe_grouped_gemm_down_combine_noalloc - moe_grouped_gemm_down_combine for callers that
+ * cannot allocate or pass a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same arguments without ws; the fp32 rows p o live in a
+ * static device array of MOE_NOALLOC_SCRATCH_BYTES held by each GPU the library runs on
+ * until the process ends, and the combine runs in as many column windows as that requires
+ * (results bit-identical to moe_grouped_gemm_down_combine). Nothing is allocated: the array's
+ * device address is looked up once per device (hipGetSymbolAddress) on the first call.
+ * Every call on one GPU shares its array, so calls that overlap on one GPU (other streams,
+ * other threads) race; calls on one stream are ordered and safe. Nothing in the array needs
+ * to start at zero: each pass writes every row the combine reads.
+ * Errors: as moe_grouped_gemm_down_combine; R_cap * min(d, 256) * 4 > MOE_NOALLOC_SCRATCH_BYTES
+ * (more rows than one 256-column window of the array holds: R_cap > 65536 for d >= 256)
+ * returns MOE_ERR_WORKSPACE before any launch; a failed symbol lookup returns MOE_ERR_HIP.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+moe_status moe_grouped_gemm_down_combine_noalloc(const void* a, const int32_t* expert_offsets,
+                                                 const float* row_gate,
+                                                 const int32_t* slot_row, int64_t T, int k,
+                                                 int E_loc, int64_t R_cap, int H, int d,
+                                                 const void* w_down, void* y,
+                                                 hipStream_t stream);
+
+/*
  * moe_expert_bwd - backward of the expert layer with dL/dy = dy ("MoE 反向"):
  *   G      = dy[row_token] . w_down[e]                        (re-dispatch of dy fused)
  *   a      = SiTU-GLU(h) recomputed exactly as in the forward epilogue

@@ -57,6 +57,8 @@ _SIGS = {
     "moe_expert_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _I64, _I, _I, _I64, _I, _I, _P, _P, _F,
                             _F, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_router_bwd": (_I, [_P, _P, _I64, _I, _P, _P]),
+    "moe_grouped_gemm_down_combine_noalloc": (_I, [_P, _P, _P, _P, _I64, _I, _I, _I64, _I, _I,
+                                                   _P, _P, _P]),
     "moe_expert_bwd_stages": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I, _I, _I64, _I,
                                    _I, _P, _P, _F, _F, _P, _P, _P, _P, _P, _SZ, _I, _P]),
     "moe_grouped_gemm_gate_up_mx": (_I, [_P, _I64, _P, _P, _I, _I64, _I, _I, _P, _F, _F, _P, _P,
@@ -297,6 +299,26 @@ def moe_grouped_gemm_down_combine(a, offsets, row_gate, slot_row, w_down, R_cap,
     _check("moe_grouped_gemm_down_combine", load().moe_grouped_gemm_down_combine(
         _ptr(a), _ptr(offsets), _ptr(row_gate), _ptr(slot_row), T, k, E_loc, R_cap, H, d,
         _ptr(w_down), _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
+    return y
+
+
+def moe_grouped_gemm_down_combine_noalloc(a, offsets, row_gate, slot_row, w_down, R_cap,
+                                          y=None, stream=None):
+    """moe_grouped_gemm_down_combine without a workspace: the fp32 rows live in the library's
+    static per-device scratch (R_cap at most 65536 for d >= 256). Calls that overlap on one GPU
+    race on that scratch."""
+    E_loc, d, H = w_down.shape
+    T, k = slot_row.shape
+    _need_rows(a, "a", torch.bfloat16, R_cap, H)
+    _need(w_down, "w_down", torch.bfloat16)
+    _need(offsets, "offsets", torch.int32, (E_loc + 1,))
+    _need_rows(row_gate, "row_gate", torch.float32, R_cap)
+    _need(slot_row, "slot_row", torch.int32)
+    y = torch.empty((T, d), dtype=torch.bfloat16, device=a.device) if y is None else y
+    _need(y, "y", torch.bfloat16, (T, d))
+    _check("moe_grouped_gemm_down_combine_noalloc", load().moe_grouped_gemm_down_combine_noalloc(
+        _ptr(a), _ptr(offsets), _ptr(row_gate), _ptr(slot_row), T, k, E_loc, R_cap, H, d,
+        _ptr(w_down), _ptr(y), _stream(stream)))
     return y
 
 

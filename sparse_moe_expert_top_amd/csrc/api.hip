@@ -79,6 +79,29 @@ static bool rows_addressable(int64_t T, int d, int H) {
   return T * w * 2 < ((int64_t)1 << 32);
 }
 
+// Scratch of moe_grouped_gemm_down_combine_noalloc: the fp32 rows p o of one column window.
+// Each GPU the library runs on holds its own copy until the process ends. In host code the
+// name `scratch` is only a stand-in for the symbol: kernels get the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per device and kept.
+static __device__ __attribute__((aligned(256))) float scratch[MOE_NOALLOC_SCRATCH_BYTES / 4];
+static void* g_scratch_ptr[128];
+
+static hipError_t static_scratch(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 128) return hipErrorInvalidDevice;
+  void* p = __atomic_load_n(&g_scratch_ptr[dev], __ATOMIC_ACQUIRE);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    __atomic_store_n(&g_scratch_ptr[dev], p, __ATOMIC_RELEASE);
+  }
+  *out = (float*)p;
+  return hipSuccess;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -289,6 +312,24 @@ moe_status moe_grouped_gemm_down_combine(const void* a, const int32_t* expert_of
                                          size_t ws_bytes, hipStream_t stream) {
   return down_combine_impl(a, expert_offsets, row_gate, slot_row, T, k, E_loc, R_cap, H, d,
                            w_down, y, (float*)ws, ws_bytes, stream);
+}
+
+moe_status moe_grouped_gemm_down_combine_noalloc(const void* a, const int32_t* expert_offsets,
+                                                 const float* row_gate,
+                                                 const int32_t* slot_row, int64_t T, int k,
+                                                 int E_loc, int64_t R_cap, int H, int d,
+                                                 const void* w_down, void* y,
+                                                 hipStream_t stream) {
+  if (R_cap < 0) return MOE_ERR_SHAPE;
+  if (R_cap * (int64_t)combine_min_cols(d > 0 ? d : 1) * 4 > (int64_t)MOE_NOALLOC_SCRATCH_BYTES)
+    return MOE_ERR_WORKSPACE;                    // rows beyond what the static scratch holds
+  float* rows = nullptr;
+  if (R_cap > 0) {
+    const hipError_t e = static_scratch(&rows);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return down_combine_impl(a, expert_offsets, row_gate, slot_row, T, k, E_loc, R_cap, H, d,
+                           w_down, y, rows, MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 static moe_status expert_bwd_impl(const void* dy, const void* x, const void* h,

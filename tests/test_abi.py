@@ -306,3 +306,17 @@ def test_expert_bwd_stages_rejects(lib):
     assert st(a2=None, a3=P) == ENULL                                  # codes without scales
     assert st(a24=10) == EWS
     assert st(a13=96) == EUNSUP
+
+
+def test_noalloc_down_combine_rejects(lib):
+    """The allocation-free down combine refuses more rows than its static scratch holds for one
+    256-column window (65536 at d >= 256), and the usual bad arguments, before any launch."""
+    P = ctypes.c_void_p(256)
+    na = lib.moe_grouped_gemm_down_combine_noalloc
+    #            a  off gate slot T  k  E_loc R_cap   H   d    w  y  stream
+    assert na(P, P, P, P, 8, 2, 4, 65537, 64, 512, P, P, None) == EWS
+    assert na(P, P, P, P, 8, 2, 4, 1 << 20, 64, 128, P, P, None) == EWS   # d < 256: 128 columns
+    assert na(P, P, P, P, 8, 2, 4, -1, 64, 512, P, P, None) == ESHAPE
+    assert na(P, P, P, P, 8, 2, 4, 0, 64, 100, P, P, None) == EUNSUP       # d % 64
+    assert na(P, None, P, P, 8, 2, 4, 0, 64, 512, P, P, None) == ENULL     # offsets
+    assert na(P, P, P, P, 8, 2, 4, 0, 64, 512, None, P, None) == ENULL     # w_down
