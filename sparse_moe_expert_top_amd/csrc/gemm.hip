@@ -159,13 +159,23 @@ __device__ __forceinline__ i16x4 ds_read_tr(const uint16_t* lds_src) {
 #define MOE_NT_F32 1
 #endif
 #ifndef MOE_NT_ROWS
-#define MOE_NT_ROWS 0
+#define MOE_NT_ROWS 1
 #endif
 __device__ __forceinline__ void st_f32(float* p, float v) {
 #if MOE_NT_F32
   __builtin_nontemporal_store(v, p);
 #else
   *p = v;
+#endif
+}
+#ifndef MOE_NT_F32ROWS
+#define MOE_NT_F32ROWS 1
+#endif
+__device__ __forceinline__ void st_f32x4(float* p, f32x4 v) {
+#if MOE_NT_F32ROWS
+  __builtin_nontemporal_store(v, (f32x4*)p);
+#else
+  *(f32x4*)p = v;
 #endif
 }
 __device__ __forceinline__ void st_row16(uint16_t* p, u32x4 v) {
@@ -205,6 +215,13 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
   uint16_t (*sB)[BN * BK] = reinterpret_cast<uint16_t (*)[BN * BK]>(ring + NS * BM * BK);
   __shared__ int s_pref[1025];
   __shared__ int s_scan[NT];
+#ifndef MOE_PREFETCH
+#define MOE_PREFETCH 0
+#endif
+  // L2 prefetch of the stage after the one being loaded (row GEMMs, 2-slot ring): one 4-byte
+  // direct-to-LDS load per 128-byte line of the stage, landing in a scratch word nobody reads.
+  constexpr bool PF = MOE_PREFETCH && !KRAG && NS == 2;
+  __shared__ uint32_t pf_trash[PF ? 64 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -368,6 +385,16 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
           gb = *(cidx_t*)(p.b_gather + r0 + kt * BK + wave_u * KPW);
       }
     };
+    // Row index of this lane's k-row in a full stage: lanes 0..31 take the first of the load's
+    // two k-rows, lanes 32..63 the second. Both candidates pass through empty asm as scalars,
+    // so the compiler selects between two registers instead of indexing the vector with a
+    // per-lane index (which it expands into a compare-and-select chain over all KPW entries).
+    auto pick_row = [&](const kidx_t& gv, auto qc) __attribute__((always_inline)) -> uint32_t {
+      constexpr int Q = decltype(qc)::value;
+      uint32_t lo = (uint32_t)gv[2 * Q], hi = (uint32_t)gv[2 * Q + 1];
+      asm volatile("" : "+s"(lo), "+s"(hi));
+      return (lane < 32) ? lo : hi;
+    };
     auto tail_row = [&](const int32_t* gather, int kr) __attribute__((always_inline)) {
       const int kg = kr;
       return (kg < Kg) ? (gather ? gather[r0 + kg] : (r0 + kg)) : -1;
@@ -381,11 +408,10 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
       } else if ((kt + 1) * BK <= Kg) {
         // full ragged-K stage: every k-row exists
         uint32_t voff[LA];
-#pragma unroll
-        for (int q = 0; q < LA; ++q)
-          voff[q] = p.a_gather ? (uint32_t)(lane < 32 ? ga[2 * q] : ga[2 * q + 1]) *
-                                         (uint32_t)(p.lda * 2) + a_off[q]
-                               : a_off[q];
+        static_for<LA>([&](auto qc) __attribute__((always_inline)) {
+          constexpr int q = decltype(qc)::value;
+          voff[q] = p.a_gather ? pick_row(ga, qc) * (uint32_t)(p.lda * 2) + a_off[q] : a_off[q];
+        });
         const uint16_t* base = p.a_gather ? p.A : p.A + (int64_t)(r0 + kt * BK) * p.lda;
         dma_saddr<LA>(lds_a, uniform_ptr(base), voff);
       } else {
@@ -405,11 +431,10 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
       else if constexpr (!KRAG) return Bg + (int64_t)kt * BK * p.ldb;
       else return p.b_gather ? p.B : p.B + (int64_t)(r0 + kt * BK) * p.ldb;
     };
-    auto b_voff = [&](int q) __attribute__((always_inline)) -> uint32_t {
+    auto b_voff = [&](auto qc) __attribute__((always_inline)) -> uint32_t {
+      constexpr int q = decltype(qc)::value;
       if constexpr (KRAG)
-        return p.b_gather ? (uint32_t)(lane < 32 ? gb[2 * q] : gb[2 * q + 1]) *
-                                    (uint32_t)(p.ldb * 2) + b_off[q]
-                          : b_off[q];
+        return p.b_gather ? pick_row(gb, qc) * (uint32_t)(p.ldb * 2) + b_off[q] : b_off[q];
       else return b_off[q];
     };
     auto b_full = [&](int kt) __attribute__((always_inline)) {
@@ -421,8 +446,9 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
       const uint32_t lds_b = ring_lds + NS * (BM * BK * 2) + slot * (BN * BK * 2) + wave_u * (LB * 1024);
       if (b_full(kt)) {
         uint32_t voff[LB];
-#pragma unroll
-        for (int q = 0; q < LB; ++q) voff[q] = b_voff(q);
+        static_for<LB>([&](auto qc) __attribute__((always_inline)) {
+          voff[decltype(qc)::value] = b_voff(qc);
+        });
         dma_saddr<LB>(lds_b, uniform_ptr(b_base(kt)), voff);
       } else {
 #pragma unroll
@@ -437,6 +463,38 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
     auto issue = [&](int kt) __attribute__((always_inline)) {
       issue_a(kt);
       issue_b(kt);
+    };
+    // Prefetch: lane (wave % 4) * 64 + lane of waves 0..3 touches A's line of that tile row,
+    // of waves 4..7 B's line (rows operand: a weight row; k-outer: 64 k-rows x 4 lines).
+    uint32_t pf_off = 0;
+    if constexpr (PF) {
+      const int idx = (wave & 3) * 64 + lane;
+      if (wave_u < 4) {
+        const int m = min(m0 + idx, Me - 1);
+        const int srow = p.a_gather ? p.a_gather[r0 + m] : m;
+        pf_off = (uint32_t)((int64_t)srow * p.lda * 2);
+      } else if constexpr (!B_KO) {
+        int wrow;
+        if constexpr (IS_GU) {
+          const int w = idx / WN, qq = idx % WN;
+          const int jj = min(j0 + w * (WN / 2) + (qq % (WN / 2)), p.H - 1);
+          wrow = (qq < WN / 2) ? jj : p.H + jj;
+        } else {
+          wrow = min(n0 + idx, p.N - 1);
+        }
+        pf_off = (uint32_t)((int64_t)wrow * p.ldb * 2);
+      } else {
+        const int col = min(n0 + (idx & 3) * 64, p.N - 64);
+        pf_off = (uint32_t)(((int64_t)(idx >> 2) * p.ldb + col) * 2);
+      }
+    }
+    const uint32_t pf_lds = PF ? __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)pf_trash) : 0u;
+    auto prefetch = [&](int kt) __attribute__((always_inline)) {
+      if constexpr (PF) {
+        const void* base = (wave_u < 4) ? (const void*)(a_base + kt * BK) : (const void*)b_base(kt);
+        dma_saddr_b32(pf_lds, uniform_ptr(base), pf_off);
+      }
     };
 
     f32x16 acc[FM][FN];
@@ -508,6 +566,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
       wait_stage(min(NS - 2, nk - 1));
       block_sync();
       if (NS - 1 < nk) issue(NS - 1);
+      if (PF && NS < nk) prefetch(NS);
       load_frags(nfc, 0, 0, fa[0], fb[0]);
       for (int kt = 0; kt < nk; ++kt) {
         const int slot = kt & (NS - 1);
@@ -517,9 +576,12 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
           mfma_step(nfc, fa[s & 1], fb[s & 1]);
         }
         if (kt + 1 < nk) {
-          wait_stage(min(NS - 2, nk - 2 - kt));
+          // with prefetch, stage kt+1's loads were followed by the prefetch of stage kt+2
+          if (PF && kt + 2 < nk) wait_vm_lgkm0<1>();
+          else wait_stage(min(NS - 2, nk - 2 - kt));
           block_sync();
           if (kt + NS < nk) issue(kt + NS);
+          if (PF && kt + NS + 1 < nk) prefetch(kt + NS + 1);
           load_frags(nfc, (kt + 1) & (NS - 1), 0, fa[0], fb[0]);
         }
         mfma_step(nfc, fa[1], fb[1]);
@@ -595,11 +657,14 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
     for (int i = 0; i < FM; ++i) {
       if (i >= nfv) break;
       const int rblk = m0 + wm * WM + i * 32;            // tile-relative row of block row 0
+      // fp32 row epilogues: lane group lane/8 takes rows 0,4,1,5,2,6,3,7 (+ 8 ps), so each
+      // 16-lane LDS read pass covers two rows in opposite bank halves
+      const int rl = (((lane >> 3) & 1) << 2) | (lane >> 4);
       float rsc[4];
       if constexpr (ROW_SCALE) {
 #pragma unroll
         for (int ps = 0; ps < 4; ++ps) {
-          const int row = rblk + ps * 8 + (lane >> 3);
+          const int row = rblk + ps * 8 + rl;
           rsc[ps] = (row < Me) ? p.row_scale[r0 + row] : 0.0f;
         }
       }
@@ -667,6 +732,31 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
             st_row16(&p.o1[r * p.ld1 + jj], av);
           }
         }
+      } else if constexpr (EPI == EPI_ROWS || EPI == EPI_ROWS_SCALED) {
+        // fp32 rows (the combine sums them in fp32 and rounds a token's sum once). The 8
+        // lanes of a row hold columns 4 cc .. 4 cc + 3 and 32 + 4 cc .. 32 + 4 cc + 3, so each
+        // of the two stores writes whole 128-byte lines of 8 rows.
+        const int cc = lane & 7;
+        const int col = n0 + wn * WN;                    // N is a multiple of 64
+        if (col < p.N) {
+#pragma unroll
+          for (int ps = 0; ps < 4; ++ps) {
+            const int row = ps * 8 + rl;
+            const f32x4 c0 = *(const f32x4*)&st[row * EPS + cc * 4];
+            const f32x4 c1 = *(const f32x4*)&st[row * EPS + 32 + cc * 4];
+            if (rblk + row < Me) {
+              float* dst = p.of + (int64_t)(r0 + rblk + row) * p.ldf + col + cc * 4;
+              if constexpr (EPI == EPI_ROWS_SCALED) {
+                const float sc = rsc[ps];
+                st_f32x4(dst, f32x4{c0[0] * sc, c0[1] * sc, c0[2] * sc, c0[3] * sc});
+                st_f32x4(dst + 32, f32x4{c1[0] * sc, c1[1] * sc, c1[2] * sc, c1[3] * sc});
+              } else {
+                st_f32x4(dst, c0);
+                st_f32x4(dst + 32, c1);
+              }
+            }
+          }
+        }
       } else {
         // lane: columns cc*8 .. cc*8+7 of row ps*8 + lane/8
         const int cc = lane & 7;
@@ -678,21 +768,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
           const f32x4 c0 = *(const f32x4*)&st[row * EPS + cc * 8];
           const f32x4 c1 = *(const f32x4*)&st[row * EPS + cc * 8 + 4];
           const float cv[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-          if constexpr (EPI == EPI_ROWS || EPI == EPI_ROWS_SCALED) {
-            // fp32 rows: the combine sums them in fp32 and rounds the token's sum once
-            if (rblk + row < Me && col < p.N) {
-              const int64_t r = r0 + rblk + row;
-              float* dst = p.of + r * p.ldf + col;
-              if constexpr (EPI == EPI_ROWS_SCALED) {
-                const float sc = rsc[ps];
-                *(f32x4*)dst = f32x4{cv[0] * sc, cv[1] * sc, cv[2] * sc, cv[3] * sc};
-                *(f32x4*)(dst + 4) = f32x4{cv[4] * sc, cv[5] * sc, cv[6] * sc, cv[7] * sc};
-              } else {
-                *(f32x4*)dst = c0;
-                *(f32x4*)(dst + 4) = c1;
-              }
-            }
-          } else if constexpr (IS_DA) {
+          if constexpr (IS_DA) {
             if (rblk + row < Me && col < p.N) {
               const int64_t r = r0 + rblk + row;
               const float pr = p.row_scale[r];
