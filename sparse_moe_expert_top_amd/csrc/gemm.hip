@@ -21,7 +21,8 @@
 //    direct-to-LDS loads (global_load_lds_dwordx4, 1 KiB per wavefront instruction), issued
 //    NS-1 stages ahead of its use; one barrier per stage, placed before the stage's last
 //    k-step, orders fills after the reads of the slot they overwrite, and the last k-step's
-//    MFMAs cover the next stage's first fragment reads.
+//    MFMAs cover the next stage's first fragment reads. dA and dX use a ping-pong form
+//    instead (32-deep stages, 4 slots, the two wavefronts of each SIMD one phase apart).
 //  * A wavefront whose 32-row fragments lie wholly past the end of a group's rows skips
 //    them (the k-loop is compiled once per count of live fragments), so the last, partly
 //    filled tile of each expert costs only the MFMAs of its live rows.
@@ -95,14 +96,16 @@ struct GemmArgs {
 };
 
 // Tile configuration: BM x BN tile, WGM x WGN wavefronts, BK-deep stages, NS-slot ring,
-// WPE = wavefronts per SIMD the kernel is compiled for.
-template <int BM_, int BN_, int WGM_, int WGN_, int BK_, int NS_, int WPE_>
+// WPE = wavefronts per SIMD the kernel is compiled for, PP = ping-pong k-loop (below).
+template <int BM_, int BN_, int WGM_, int WGN_, int BK_, int NS_, int WPE_, bool PP_ = false>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, BK = BK_, NS = NS_;
   static constexpr int WPE = WPE_;
+  static constexpr bool PP = PP_;
   static constexpr int NT = 64 * WGM * WGN;
 };
-using CfgBig = TileCfg<256, 256, 2, 4, 64, 2, 2>;     // 8 waves, 128 KiB ring, 1 WG per CU
+using CfgPP = TileCfg<256, 256, 2, 4, 32, 4, 2, true>;  // 8 waves, 4 x 32 KiB ring, ping-pong
+using CfgBig = TileCfg<256, 256, 2, 4, 64, 2, 2>;     // 8 waves, 2 x 64 KiB ring
 using CfgMid = TileCfg<128, 256, 2, 4, 64, 2, 2>;     // 8 waves, 96 KiB ring
 using CfgSmall = TileCfg<128, 128, 2, 2, 32, 4, 2>;   // 4 waves, 64 KiB ring, 2 WG per CU
 
@@ -208,6 +211,7 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
   constexpr bool HMX = (EPI == EPI_GATEUP_MX || EPI == EPI_DA_MX);
   static_assert(!IS_GU || (FN % 2 == 0), "gate/linear pairs");
   static_assert(BK == 32 || BK == 64, "stage depth");
+  static_assert(!C::PP || (NT == 512 && NS == 4 && BK == 32), "ping-pong geometry");
 
   // One LDS ring for both operands; after the k-loop it doubles as the epilogue's staging.
   __shared__ __attribute__((aligned(1024))) uint16_t ring[NS * (BM + BN) * BK];
@@ -555,8 +559,48 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
     // stage kt+1 (so after the barrier all of stage kt+1 is in LDS). The MFMAs of the last
     // k-step then cover the refill's issue and the latency of stage kt+1's first fragment
     // reads, instead of leaving the matrix core idle across the barrier.
+    //
+    // Ping-pong form (C::PP: 32-deep stages, 4-slot ring, 8 wavefronts). Wavefronts w and
+    // w + 4 share a SIMD. The groups {0..3} and {4..7} run one phase apart, so on every SIMD
+    // one wavefront issues MFMAs while the other issues loads and LDS reads. A stage j is a
+    // memory phase (issue stage j+3's loads, read both k-steps' fragments of stage j) and a
+    // math phase (its MFMAs), each ended by a barrier; group 1 starts one barrier late and
+    // group 0 ends one barrier late, so both execute the same barriers. The barriers order:
+    //  * the refill with stage j+3 after all reads of stage j-1, whose slot it reuses: group
+    //    0 read it before its own MFMAs of stage j-1; group 1 read it in the phase just
+    //    before and waits for those reads before that phase's barrier;
+    //  * the reads of stage j+1 after all of its loads: each wavefront waits for its own
+    //    loads of stage j+1 before the barrier that ends group 1's memory phase of stage j.
     static_assert(KS % 2 == 0, "fragment double buffer alternates within a stage");
-    auto kloop = [&](auto nfc) __attribute__((always_inline)) {
+    const int pgrp = C::PP ? (wave_u >> 2) : 0;
+    auto kloop_pp = [&](auto nfc) __attribute__((always_inline)) {
+      bf16x8 fa[2][FM], fb[2][FN];
+      fetch_a(0);
+      fetch_b(0);
+#pragma unroll
+      for (int st = 0; st < 3; ++st)
+        if (st < nk) issue(st);
+      wait_stage(min(2, nk - 1));
+      block_sync();
+      if (pgrp) block_sync();
+      for (int j = 0; j < nk; ++j) {
+        const int slot = j & 3;
+        if (j + 3 < nk) issue(j + 3);
+        load_frags(nfc, slot, 0, fa[0], fb[0]);
+        load_frags(nfc, slot, 1, fa[1], fb[1]);
+        if (pgrp) wait_stage(min(2, nk - 2 - j));
+        block_sync();
+        mfma_step(nfc, fa[0], fb[0]);
+        mfma_step(nfc, fa[1], fb[1]);
+        if (!pgrp) wait_stage(min(2, nk - 2 - j));
+        block_sync();
+      }
+      if (!pgrp) block_sync();
+      // every wave is done with the ring before the epilogue stages through it
+      wait_vm_lgkm0<0>();
+      block_sync();
+    };
+    auto kloop_std = [&](auto nfc) __attribute__((always_inline)) {
       bf16x8 fa[2][FM], fb[2][FN];
       fetch_a(0);
       fetch_b(0);
@@ -589,6 +633,10 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
       // every wave is done with the ring before the epilogue stages through it
       wait_vm_lgkm0<0>();
       block_sync();
+    };
+    auto kloop = [&](auto nfc) __attribute__((always_inline)) {
+      if constexpr (C::PP) kloop_pp(nfc);
+      else kloop_std(nfc);
     };
     // Row GEMMs: a tile at the end of a group may hold only a few rows; this wave's
     // fragments wholly past the group's last row are skipped (a wave-uniform count).
@@ -874,10 +922,10 @@ static hipError_t run_gemm(const GemmArgs& args, int64_t max_tiles, hipStream_t 
 #define MOE_CFG_DN CfgBig
 #endif
 #ifndef MOE_CFG_DA
-#define MOE_CFG_DA CfgBig
+#define MOE_CFG_DA CfgPP
 #endif
 #ifndef MOE_CFG_DX
-#define MOE_CFG_DX CfgBig
+#define MOE_CFG_DX CfgPP
 #endif
 #ifndef MOE_CFG_WD
 #define MOE_CFG_WD CfgBig
