@@ -66,6 +66,9 @@ def parse():
                     help="print the digest of the kernel sources and exit")
     ap.add_argument("--blas-reference", action="store_true",
                     help="only time torch's bf16 GEMMs (hipBLASLt) on the layer's shapes, as context")
+    ap.add_argument("--blas-rows", type=int, default=16456,
+                    help="routed rows R for --blas-reference (16456: the shard workload; "
+                         "1572864: the large-context workload)")
     return ap.parse_args()
 
 
@@ -303,7 +306,7 @@ def main():
     torch.cuda.set_device(0)
     cfg = LAYER_CONFIGS[args.workload]
     if args.blas_reference:
-        blas_reference(cfg, 16456)
+        blas_reference(cfg, args.blas_rows)
         return
     inp, t = load_workload(cfg, torch)
     input_gb = sum(v.numel() * v.element_size() for v in t.values()) / 1e9

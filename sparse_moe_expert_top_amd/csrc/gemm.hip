@@ -936,6 +936,9 @@ static hipError_t run_gemm(const GemmArgs& args, int64_t max_tiles, hipStream_t 
 #ifndef MOE_GROUP_M
 #define MOE_GROUP_M 4
 #endif
+#ifndef MOE_GROUP_M_W                 // the weight gradients' super-row height
+#define MOE_GROUP_M_W 8
+#endif
 using CGU = MOE_CFG_GU;
 using CDN = MOE_CFG_DN;
 using CDA = MOE_CFG_DA;
@@ -1044,6 +1047,7 @@ hipError_t launch_gemm_dw_down(const uint16_t* dy, const int32_t* row_token,
   GemmArgs p = blank_args();
   p.A = dy; p.lda = d; p.a_gather = row_token;                // A(m, k=r) = dy[tok(r)][m]
   p.B = pa; p.ldb = H;                                        // B(n, k=r) = pa[r][n]
+  p.group_m = MOE_GROUP_M_W;
   p.offsets = offsets; p.G = E_loc;
   p.M = d; p.N = H;
   p.m_tiles = (d + CWD::BM - 1) / CWD::BM;
@@ -1058,6 +1062,7 @@ hipError_t launch_gemm_dw_gu(const uint16_t* dh, const uint16_t* x, const int32_
   GemmArgs p = blank_args();
   p.A = dh; p.lda = 2 * H;                                    // A(m, k=r) = dh[r][m]
   p.B = x; p.ldb = d; p.b_gather = row_token;                 // B(n, k=r) = x[tok(r)][n]
+  p.group_m = MOE_GROUP_M_W;
   p.offsets = offsets; p.G = E_loc;
   p.M = 2 * H; p.N = d;
   p.m_tiles = (2 * H + CWG::BM - 1) / CWG::BM;

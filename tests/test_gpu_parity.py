@@ -467,7 +467,7 @@ def check_h_codes(got_c, got_s, h_ref, what):
     assert same_c >= 0.999 and same_s >= 0.999, (what, same_c, same_s)
 
 
-def compare_sampled(m, cfg, n_tok=48, n_exp=3, n_col=6, seed=0, h_store="bf16"):
+def compare_sampled(m, cfg, n_tok=128, n_exp=4, n_col=14, seed=0, h_store="bf16"):
     """Sampled comparison at full size: tokens (all their local rows), their rows' h and a,
     and the weight-gradient columns of sampled experts (incl. empty ones). h_store="mxfp8"
     runs the MXFP8-store path; its stored codes are checked within a bound and its weight-
