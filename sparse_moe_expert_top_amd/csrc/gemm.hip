@@ -105,9 +105,7 @@ struct TileCfg {
   static constexpr int NT = 64 * WGM * WGN;
 };
 using CfgPP = TileCfg<256, 256, 2, 4, 32, 4, 2, true>;  // 8 waves, 4 x 32 KiB ring, ping-pong
-using CfgBig = TileCfg<256, 256, 2, 4, 64, 2, 2>;     // 8 waves, 2 x 64 KiB ring
-using CfgMid = TileCfg<128, 256, 2, 4, 64, 2, 2>;     // 8 waves, 96 KiB ring
-using CfgSmall = TileCfg<128, 128, 2, 2, 32, 4, 2>;   // 4 waves, 64 KiB ring, 2 WG per CU
+using CfgBig = TileCfg<256, 256, 2, 4, 64, 2, 2>;        // 8 waves, 2 x 64 KiB ring
 
 // ---------------------------------------------------------------------------- LDS stages
 // LDS on gfx950 serves a 16-byte-per-lane read in 256-byte passes (64 banks of 4 bytes), so
@@ -219,13 +217,6 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
   uint16_t (*sB)[BN * BK] = reinterpret_cast<uint16_t (*)[BN * BK]>(ring + NS * BM * BK);
   __shared__ int s_pref[1025];
   __shared__ int s_scan[NT];
-#ifndef MOE_PREFETCH
-#define MOE_PREFETCH 0
-#endif
-  // L2 prefetch of the stage after the one being loaded (row GEMMs, 2-slot ring): one 4-byte
-  // direct-to-LDS load per 128-byte line of the stage, landing in a scratch word nobody reads.
-  constexpr bool PF = MOE_PREFETCH && !KRAG && NS == 2;
-  __shared__ uint32_t pf_trash[PF ? 64 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -468,39 +459,6 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
       issue_a(kt);
       issue_b(kt);
     };
-    // Prefetch: lane (wave % 4) * 64 + lane of waves 0..3 touches A's line of that tile row,
-    // of waves 4..7 B's line (rows operand: a weight row; k-outer: 64 k-rows x 4 lines).
-    uint32_t pf_off = 0;
-    if constexpr (PF) {
-      const int idx = (wave & 3) * 64 + lane;
-      if (wave_u < 4) {
-        const int m = min(m0 + idx, Me - 1);
-        const int srow = p.a_gather ? p.a_gather[r0 + m] : m;
-        pf_off = (uint32_t)((int64_t)srow * p.lda * 2);
-      } else if constexpr (!B_KO) {
-        int wrow;
-        if constexpr (IS_GU) {
-          const int w = idx / WN, qq = idx % WN;
-          const int jj = min(j0 + w * (WN / 2) + (qq % (WN / 2)), p.H - 1);
-          wrow = (qq < WN / 2) ? jj : p.H + jj;
-        } else {
-          wrow = min(n0 + idx, p.N - 1);
-        }
-        pf_off = (uint32_t)((int64_t)wrow * p.ldb * 2);
-      } else {
-        const int col = min(n0 + (idx & 3) * 64, p.N - 64);
-        pf_off = (uint32_t)(((int64_t)(idx >> 2) * p.ldb + col) * 2);
-      }
-    }
-    const uint32_t pf_lds = PF ? __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)pf_trash) : 0u;
-    auto prefetch = [&](int kt) __attribute__((always_inline)) {
-      if constexpr (PF) {
-        const void* base = (wave_u < 4) ? (const void*)(a_base + kt * BK) : (const void*)b_base(kt);
-        dma_saddr_b32(pf_lds, uniform_ptr(base), pf_off);
-      }
-    };
-
     f32x16 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -610,7 +568,6 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
       wait_stage(min(NS - 2, nk - 1));
       block_sync();
       if (NS - 1 < nk) issue(NS - 1);
-      if (PF && NS < nk) prefetch(NS);
       load_frags(nfc, 0, 0, fa[0], fb[0]);
       for (int kt = 0; kt < nk; ++kt) {
         const int slot = kt & (NS - 1);
@@ -620,12 +577,9 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
           mfma_step(nfc, fa[s & 1], fb[s & 1]);
         }
         if (kt + 1 < nk) {
-          // with prefetch, stage kt+1's loads were followed by the prefetch of stage kt+2
-          if (PF && kt + 2 < nk) wait_vm_lgkm0<1>();
-          else wait_stage(min(NS - 2, nk - 2 - kt));
+          wait_stage(min(NS - 2, nk - 2 - kt));
           block_sync();
           if (kt + NS < nk) issue(kt + NS);
-          if (PF && kt + NS + 1 < nk) prefetch(kt + NS + 1);
           load_frags(nfc, (kt + 1) & (NS - 1), 0, fa[0], fb[0]);
         }
         mfma_step(nfc, fa[1], fb[1]);
