@@ -171,9 +171,13 @@ def cpu_baseline(cfg, inp, target_s):
     expert (its rows are independent of the rest). n is sized from a warm timing so the run
     takes about target_s seconds."""
     import oracle
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"] or threadpool_info()
+        threads = max((p.get("num_threads", 1) for p in pools), default=1)
+        blas = ",".join(sorted({f"{p.get('internal_api', '?')} {p.get('version', '')}".strip()
+                                for p in pools})) or blas
     except Exception:                                     # pragma: no cover
         threads = len(os.sched_getaffinity(0))
     idx, gates = oracle.route_topk(inp["logits"], cfg.k)
@@ -207,10 +211,53 @@ def cpu_baseline(cfg, inp, target_s):
     dt = run(n)
     flop = 18.0 * n * cfg.d * cfg.H
     return dict(value=flop / dt / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
+                host_cpus=len(os.sched_getaffinity(0)), blas=blas,
                 sample=f"fp64 oracle forward+backward of the first {n} routed rows of local "
                        f"expert {e0} (of {n_e}; {perm['R']} rows in all) of the same input, as "
                        f"a layer of those {n} tokens; {dt:.1f} s",
                 seconds=round(dt, 2))
+
+
+def streaming_leg(moe, cfg, t, R, torch, iters=20, warmup=3):
+    """Route and permute of the workload, each timed alone with HIP events (median of
+    `iters` after `warmup`), the Infinity Cache flushed by a 1 GiB write before each launch.
+    Algorithmic bytes: route 4TE + 8Tk (logits in; indices and gates out), permute
+    12R + 12Tk (indices and gates in; slot map, row token, gate out; offsets aside)."""
+    stream = torch.cuda.current_stream()
+    T, E, k = cfg.T, cfg.E, cfg.k
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gates = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    perm = dict(offsets=torch.empty(cfg.E_loc + 1, dtype=torch.int32, device="cuda"),
+                row_token=torch.empty(max(R, 1), dtype=torch.int32, device="cuda"),
+                row_gate=torch.empty(max(R, 1), dtype=torch.float32, device="cuda"),
+                slot_row=torch.empty((T, k), dtype=torch.int32, device="cuda"),
+                status=torch.empty(1, dtype=torch.int32, device="cuda"))
+    ws = torch.empty(max(moe.workspace_size(moe.MOE_WS_PERMUTE, T=T, E_loc=cfg.E_loc), 256),
+                     dtype=torch.uint8, device="cuda")
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    ops = {"route": lambda: moe.moe_route_topk(t["logits"], k, topk_idx=idx, gates=gates),
+           "permute": lambda: moe.moe_permute(idx, gates, cfg.e_lo, cfg.E_loc, R, out=perm, ws=ws)}
+    by = {"route": 4.0 * T * E + 8.0 * T * k, "permute": 12.0 * R + 12.0 * T * k}
+    out = {}
+    for name, fn in ops.items():
+        ms = []
+        for i in range(warmup + iters):
+            flush.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if i >= warmup:
+                ms.append(e0.elapsed_time(e1))
+        m = float(np.median(ms))
+        out[name] = {"us": round(m * 1e3, 1), "algorithmic_bytes": by[name],
+                     "GB/s": round(by[name] / (m * 1e-3) / 1e9, 1),
+                     "frac_hbm": round(by[name] / (m * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    assert int(perm["offsets"][-1].item()) == R
+    del flush, idx, gates, perm, ws
+    torch.cuda.empty_cache()
+    return out
 
 
 def load_workload(cfg, torch):
@@ -314,6 +361,8 @@ def main():
     log(f"{cfg.name}: {args.warmup} warm-up + {args.steps} timed steps")
     R, ms_step, stage_ms, peak_gb = layer_leg(moe, cfg, t, args.steps, args.warmup,
                                               args.combine_passes, torch)
+    log(f"{cfg.name}: route and permute alone")
+    streaming = streaming_leg(moe, cfg, t, R, torch)
     rdh = float(R) * cfg.d * cfg.H
     flop_step = 18.0 * rdh
     value = flop_step / (ms_step * 1e-3) / 1e12
@@ -338,6 +387,7 @@ def main():
                      "avg_launch_ms": round(stage_ms[dom], 4), "flop_per_launch": dom_flop,
                      "traffic": None},
         "stages": stages,
+        "streaming": streaming,
         "peak_hbm_GB": round(peak_gb, 2),
         "inputs_and_weights_GB": round(input_gb, 2),
         "saved_activation_GB": round((R * 2 * cfg.H * 2 + cfg.T * cfg.d * 2) / 1e9, 3),
