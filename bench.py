@@ -54,6 +54,10 @@ def parse():
     ap.add_argument("--workload", default="large")
     ap.add_argument("--secondary", default="shard",
                     help="second layer workload reported as an extra key ('none' to skip)")
+    ap.add_argument("--bwd-passes", type=int, default=0,
+                    help="column windows of the backward's dX combine (0: LayerBuffers' "
+                         "default, the fewest that keep the backward within the forward's "
+                         "memory when that saves 1 GiB or more)")
     ap.add_argument("--combine-passes", type=int, default=1,
                     help="passes over the output columns per combine (less fp32 row memory)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -305,16 +309,18 @@ def timed_steps(moe, buf, t, steps, warmup, torch):
     return ms_step, stage_ms
 
 
-def layer_leg(moe, cfg, t, steps, warmup, passes, torch, h_store="bf16"):
+def layer_leg(moe, cfg, t, steps, warmup, passes, torch, h_store="bf16", bwd_passes=0):
     shape = moe.LayerShape(T=cfg.T, E=cfg.E, k=cfg.k, e_lo=cfg.e_lo, E_loc=cfg.E_loc, d=cfg.d,
                            H=cfg.H, beta=cfg.beta, linear_beta=cfg.linear_beta)
     R = moe.LayerBuffers.routed_rows(shape, t["logits"])
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
-    buf = moe.LayerBuffers(shape, R_cap=R, h_store=h_store, combine_passes=passes)
+    buf = moe.LayerBuffers(shape, R_cap=R, h_store=h_store, combine_passes=passes,
+                           bwd_passes=bwd_passes or None)
     ms_step, stage_ms = timed_steps(moe, buf, t, steps, warmup, torch)
     assert buf.rows() == R and not buf.overflowed()
     peak = torch.cuda.max_memory_allocated() / 1e9
+    layer_leg.bwd_passes = buf.bwd_passes
     del buf
     torch.cuda.empty_cache()
     return R, ms_step, stage_ms, peak
@@ -360,7 +366,9 @@ def main():
 
     log(f"{cfg.name}: {args.warmup} warm-up + {args.steps} timed steps")
     R, ms_step, stage_ms, peak_gb = layer_leg(moe, cfg, t, args.steps, args.warmup,
-                                              args.combine_passes, torch)
+                                              args.combine_passes, torch,
+                                              bwd_passes=args.bwd_passes)
+    bwd_passes = layer_leg.bwd_passes
     log(f"{cfg.name}: route and permute alone")
     streaming = streaming_leg(moe, cfg, t, R, torch)
     rdh = float(R) * cfg.d * cfg.H
@@ -379,7 +387,7 @@ def main():
         "config": {"workload": f"{cfg.name}: {cfg.note}; T={cfg.T} d={cfg.d} H={cfg.H} "
                                f"E={cfg.E} k={cfg.k} local experts {cfg.e_lo}..{cfg.e_lo + cfg.E_loc - 1}",
                    "routed_rows": R, "flop_per_step": flop_step, "row_capacity": R,
-                   "combine_passes": args.combine_passes},
+                   "combine_passes": args.combine_passes, "bwd_combine_passes": bwd_passes},
         "mfma_frac": round(value / PEAK_BF16_TFLOPS, 4),
         "roofline": {"kernel": f"{dom}: {dict((n, w) for n, w, _ in STAGES)[dom]}",
                      "bound": "mfma", "achieved": round(dom_tf, 2), "peak": PEAK_BF16_TFLOPS,
@@ -410,7 +418,8 @@ def main():
         log(f"{cfg.name}: MXFP8-store steps")
         n_mx = max(1, args.steps // 2)
         _, ms_mx, _, peak_mx = layer_leg(moe, cfg, t, n_mx, max(1, args.warmup // 2),
-                                         args.combine_passes, torch, h_store="mxfp8")
+                                         args.combine_passes, torch, h_store="mxfp8",
+                                         bwd_passes=args.bwd_passes)
         out["mxfp8_h"] = {"ms_per_step": round(ms_mx, 4),
                           "value": round(flop_step / (ms_mx * 1e-3) / 1e12, 2),
                           "saved_activation_GB": round((R * 2 * cfg.H * (1 + 1 / 32) + cfg.T * cfg.d * 2) / 1e9, 3),
@@ -473,7 +482,7 @@ def main():
         _, t2 = load_workload(c2, torch)
         log(f"{c2.name}: {args.warmup} warm-up + {args.steps} timed steps")
         R2, ms2, st2, peak2 = layer_leg(moe, c2, t2, args.steps, args.warmup,
-                                        args.combine_passes, torch)
+                                        args.combine_passes, torch, bwd_passes=args.bwd_passes)
         out[c2.name] = {"workload": f"{c2.name}: {c2.note}", "routed_rows": R2,
                         "ms_per_step": round(ms2, 4),
                         "value": round(18.0 * R2 * c2.d * c2.H / (ms2 * 1e-3) / 1e12, 2),
