@@ -11,9 +11,9 @@
 // takes KU chunks 256 apart and finds each chunk's row and column with one 32-bit division
 // by the chunks per row, so nothing is set up per thread beyond that. Launches are split by
 // rows so each covers fewer than 2^32 chunks. No memory beyond the inputs and outputs is
-// used, whatever R. Measured on MI355X at R = 131072, H = 3072: 5.5-5.7 TB/s forward
-// (KU = 4) and 6.0 TB/s backward (KU = 2), against 5.4-5.6 TB/s for a grid-stride walk of
-// 256 workgroups per CU; plain (temporal) loads cost 5-10 %.
+// used, whatever R. Measured on MI355X at R = 131072, H = 3072: 5.5-5.8 TB/s forward
+// (KU = 4) and 5.8-5.9 TB/s backward (KU = 2), against 5.3-5.6 TB/s for a grid-stride walk
+// of 256 workgroups per CU; plain (temporal) loads cost 5-10 %.
 #include <hip/hip_runtime.h>
 #include <stdlib.h>
 
