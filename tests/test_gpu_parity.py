@@ -369,6 +369,33 @@ def test_layer_full(moe, name):
         assert not bool(buf.dw_gu.any()) and not bool(buf.dw_down.any())
 
 
+def random_layer_configs(n=32, seed=7):
+    """Seeded small shapes inside the library's envelope (d, H multiples of 64; k <= E):
+    ragged N tiles of every GEMM, K extents of 2..18 stages of 32, 1..40 experts with
+    uneven rows, local windows anywhere in the expert range."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([64, 128, 192, 320, 448, 576]))
+        H = int(rng.choice([64, 128, 192, 320, 448, 576]))
+        E = int(rng.integers(1, 41))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        E_loc = int(rng.integers(1, E + 1))
+        e_lo = int(rng.integers(0, E - E_loc + 1))
+        T = int(rng.choice([int(rng.integers(1, 16)), int(rng.integers(16, 1500))]))
+        bias = "zipf" if rng.random() < 0.3 else None
+        out.append(LayerConfig(f"rand{i}", T=T, d=d, H=H, E=E, k=k, e_lo=e_lo, E_loc=E_loc,
+                               bias=bias))
+    return out
+
+
+@pytest.mark.parametrize("cfg", random_layer_configs(), ids=lambda c: c.name)
+def test_layer_random_shapes(moe, cfg):
+    """Every element of y, dx, h, a, dW and dp against the oracle on seeded random shapes."""
+    say(f"layer random {cfg}")
+    compare_full(moe, cfg, layer_inputs(cfg, seed=1))
+
+
 def test_layer_exact_capacity(moe):
     """R_cap equal to the routed rows (the tightest legal buffers), found on the device."""
     inp = layer_inputs(MID, seed=1)
