@@ -12,7 +12,8 @@
 namespace moe {
 
 // ------------------------------------------------------------------------------ routing
-// One wavefront per token; lane l holds the logits of experts l, l+64, ... . Every logit
+// Up to 32 experts, one lane per token (route_topk_lane_kernel below); otherwise one
+// wavefront per token, lane l holding the logits of experts l, l+64, ... . Every logit
 // becomes a 64-bit key whose order is the routing order: the high word is the fp32 value
 // bits mapped to an unsigned order (-0 -> +0 first, so the two zeros tie), the low word is the
 // complement of the expert index (equal values: lower index first). Keys are unique, so
@@ -161,6 +162,79 @@ __global__ __launch_bounds__(256, 5) void route_topk_kernel(const float* __restr
   }
 }
 
+// Routing for E <= EM <= 32, one lane per token: the token's E logits become the same order
+// keys as above; a key's slot is the number of the token's keys above it (keys are unique),
+// so the k largest go straight to their slots, and the softmax takes its maximum, the value
+// of slot 0, from the largest key (keys past E read as 0, below every real key). A block's
+// 256 rows of logits, and its [256, k] outputs, are contiguous in memory, so both move
+// between HBM and LDS as whole contiguous ranges and each lane works from LDS.
+template <int EM>
+__global__ __launch_bounds__(256) void route_topk_lane_kernel(const float* __restrict__ logits,
+                                                              int64_t T, int E, int k,
+                                                              int32_t* __restrict__ idx_out,
+                                                              float* __restrict__ gates_out) {
+  __shared__ float s_val[256 * EM];
+  __shared__ int32_t s_idx[256 * EM];
+  const int tid = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * 256;
+  const int rows = (int)min((int64_t)256, T - t0);
+  const int n_in = rows * E;
+  const float* src = logits + t0 * E;
+  // every load issued before any LDS store (a guarded load-store pair per element would wait
+  // out one memory round trip each); indices past the block's range re-read its last element
+  float in[EM];
+#pragma unroll
+  for (int j = 0; j < EM; ++j) in[j] = src[min(tid + 256 * j, n_in - 1)];
+#pragma unroll
+  for (int j = 0; j < EM; ++j) {
+    const int i = tid + 256 * j;
+    if (i < n_in) s_val[i] = in[j];
+  }
+  __syncthreads();
+  int slot[EM];
+  float ex[EM];
+  float sum = 0.0f;
+  if (tid < rows) {
+    uint64_t key[EM];
+    uint64_t kmax = 0;
+#pragma unroll
+    for (int e = 0; e < EM; ++e) {
+      key[e] = (e < E) ? route_key(s_val[tid * E + e], e) : 0ull;
+      kmax = key[e] > kmax ? key[e] : kmax;
+    }
+    const float m = key_value(kmax);
+#pragma unroll
+    for (int i = 0; i < EM; ++i) {
+      int r = 0;
+#pragma unroll
+      for (int j = 0; j < EM; ++j) r += (key[j] > key[i]) ? 1 : 0;
+      slot[i] = (i < E && r < k) ? r : -1;
+      ex[i] = (slot[i] >= 0) ? expf(key_value(key[i]) - m) : 0.0f;
+      sum += ex[i];
+    }
+  }
+  __syncthreads();                                   // every lane is done reading the logits
+  if (tid < rows) {
+#pragma unroll
+    for (int i = 0; i < EM; ++i) {
+      if (slot[i] >= 0) {
+        s_idx[tid * k + slot[i]] = i;
+        s_val[tid * k + slot[i]] = ex[i] / sum;
+      }
+    }
+  }
+  __syncthreads();
+  const int n_out = rows * k;
+#pragma unroll
+  for (int j = 0; j < EM; ++j) {
+    const int i = tid + 256 * j;
+    if (i < n_out) {
+      idx_out[t0 * k + i] = s_idx[i];
+      gates_out[t0 * k + i] = s_val[i];
+    }
+  }
+}
+
 // Launches route_topk_kernel<nv> for the runtime nv in [NV, 16].
 template <int NV>
 static void route_launch_nv(int nv, dim3 grid, const float* logits, int64_t T, int E, int k,
@@ -176,6 +250,16 @@ static void route_launch_nv(int nv, dim3 grid, const float* logits, int64_t T, i
 hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int32_t* idx,
                              float* gates, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  if (E <= 32) {
+    const dim3 grid((unsigned)((T + 255) / 256));
+    if (E <= 8)
+      hipLaunchKernelGGL(route_topk_lane_kernel<8>, grid, dim3(256), 0, s, logits, T, E, k, idx, gates);
+    else if (E <= 16)
+      hipLaunchKernelGGL(route_topk_lane_kernel<16>, grid, dim3(256), 0, s, logits, T, E, k, idx, gates);
+    else
+      hipLaunchKernelGGL(route_topk_lane_kernel<32>, grid, dim3(256), 0, s, logits, T, E, k, idx, gates);
+    return hipGetLastError();
+  }
   const int nv = (E + 63) / 64;
   const int64_t waves_needed = T;
   int64_t blocks = (waves_needed + 3) / 4;

@@ -238,7 +238,10 @@ def test_route_ties(moe):
 
 
 @pytest.mark.parametrize("T,E,k", [(1000, 1024, 32), (777, 1000, 16), (300, 65, 1), (300, 64, 32),
-                                   (500, 100, 32), (257, 896, 16), (129, 33, 33 - 1)])
+                                   (500, 100, 32), (257, 896, 16), (129, 33, 33 - 1),
+                                   # E <= 32: one lane per token
+                                   (600, 28, 16), (300, 32, 32), (257, 1, 1), (300, 7, 3),
+                                   (300, 17, 17), (100, 16, 8), (70, 9, 9), (1000, 8, 2)])
 def test_route_shapes(moe, T, E, k):
     """Envelope edges of the router: E not a multiple of 64, E = 1024, k = 1 and k = 32, and
     rows that force the many-ties path (all equal; few distinct levels), next to rows with
