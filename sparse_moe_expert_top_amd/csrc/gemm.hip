@@ -812,8 +812,8 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
                   situ_bwd<B4>(hgv(2 * q + 1), hlv(2 * q + 1), pr * cv[2 * q + 1], p.sc, a1, dg1,
                                dl1);
                   const float ab0 = round_bf16(a0), ab1 = round_bf16(a1);
-                  acc_p += cv[2 * q] * ab0;
-                  acc_p += cv[2 * q + 1] * ab1;
+                  acc_p = fmaf(cv[2 * q], ab0, acc_p);
+                  acc_p = fmaf(cv[2 * q + 1], ab1, acc_p);
                   og[q] = pack_bf16x2(dg0, dg1);
                   ol[q] = pack_bf16x2(dl0, dl1);
                   oa[q] = pack_bf16x2(pr * ab0, pr * ab1);

@@ -9,8 +9,11 @@
 // 16-byte non-temporal loads, keeps all fp32 intermediates in registers and writes the
 // bf16 result with 16-byte non-temporal stores. One launch covers every chunk once: a thread
 // takes KU chunks 256 apart and finds each chunk's row and column with one 32-bit division
-// by the chunks per row, so nothing is set up per thread beyond that. Launches are split by
-// rows so each covers fewer than 2^32 chunks. No memory beyond the inputs and outputs is
+// by the chunks per row, so nothing is set up per thread beyond that. Chunk indices past the
+// end are clamped to the last chunk, so every lane loads, computes and stores without a
+// branch: the lanes of the last block that run past the end rewrite the last chunk with the
+// same bytes its own lane writes. Launches are split by rows so each covers fewer than 2^32
+// chunks. No memory beyond the inputs and outputs is
 // used, whatever R. Measured on MI355X at R = 131072, H = 3072: 5.5-5.8 TB/s forward
 // (KU = 4) and 5.8-5.9 TB/s backward (KU = 2), against 5.3-5.6 TB/s for a grid-stride walk
 // of 256 workgroups per CU; plain (temporal) loads cost 5-10 %.
@@ -60,18 +63,16 @@ __global__ __launch_bounds__(256) void situ_fwd_kernel(const uint16_t* __restric
   uint32_t rr[KU], cc[KU];
 #pragma unroll
   for (int u = 0; u < KU; ++u) {
-    const uint32_t i = i0 + 256u * u;
+    const uint32_t i = min(i0 + 256u * u, n - 1u);
     rr[u] = i / hc;
     cc[u] = i - rr[u] * hc;
-    if (i < n) {
-      const uint16_t* hr = h + (int64_t)rr[u] * (2 * H) + 8 * cc[u];
-      g[u] = ld16(hr);
-      l[u] = ld16(hr + H);
-    }
+    const uint16_t* hr = h + (int64_t)rr[u] * (2 * H) + 8 * cc[u];
+    g[u] = ld16(hr);
+    l[u] = ld16(hr + H);
   }
+  __builtin_amdgcn_sched_barrier(0);   // every load is issued before the first use
 #pragma unroll
   for (int u = 0; u < KU; ++u) {
-    if (i0 + 256u * u >= n) break;
     u32x4 o;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -94,19 +95,17 @@ __global__ __launch_bounds__(256) void situ_bwd_kernel(const uint16_t* __restric
   uint32_t rr[KU], cc[KU];
 #pragma unroll
   for (int u = 0; u < KU; ++u) {
-    const uint32_t i = i0 + 256u * u;
+    const uint32_t i = min(i0 + 256u * u, n - 1u);
     rr[u] = i / hc;
     cc[u] = i - rr[u] * hc;
-    if (i < n) {
-      const int64_t hoff = (int64_t)rr[u] * (2 * H) + 8 * cc[u];
-      g[u] = ld16(h + hoff);
-      l[u] = ld16(h + hoff + H);
-      d[u] = ld16(da + (int64_t)rr[u] * H + 8 * cc[u]);
-    }
+    const int64_t hoff = (int64_t)rr[u] * (2 * H) + 8 * cc[u];
+    g[u] = ld16(h + hoff);
+    l[u] = ld16(h + hoff + H);
+    d[u] = ld16(da + (int64_t)rr[u] * H + 8 * cc[u]);
   }
+  __builtin_amdgcn_sched_barrier(0);   // every load is issued before the first use
 #pragma unroll
   for (int u = 0; u < KU; ++u) {
-    if (i0 + 256u * u >= n) break;
     u32x4 og, ol;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
