@@ -13,10 +13,10 @@
 // end are clamped to the last chunk, so every lane loads, computes and stores without a
 // branch: the lanes of the last block that run past the end rewrite the last chunk with the
 // same bytes its own lane writes. Launches are split by rows so each covers fewer than 2^32
-// chunks. No memory beyond the inputs and outputs is
-// used, whatever R. Measured on MI355X at R = 131072, H = 3072: 5.5-5.8 TB/s forward
-// (KU = 4) and 5.8-5.9 TB/s backward (KU = 2), against 5.3-5.6 TB/s for a grid-stride walk
-// of 256 workgroups per CU; plain (temporal) loads cost 5-10 %.
+// chunks. No memory beyond the inputs and outputs is used, whatever R. Measured on MI355X at
+// R = 131072, H = 3072: 5.9-6.1 TB/s forward and 6.1-6.2 TB/s backward. A grid-stride walk
+// of 256 workgroups per CU measured 3-6 % slower than one launch over every chunk, and plain
+// (temporal) loads 5-10 % slower.
 #include <hip/hip_runtime.h>
 #include <stdlib.h>
 
@@ -48,10 +48,17 @@ __device__ __forceinline__ void st16(u32x4 v, uint16_t* p) {
 #endif
 }
 
-// Chunks per thread: the forward's four loads and the backward's six per chunk pair keep
-// enough bytes in flight at these counts (measured best of 2 and 4 for each).
-constexpr int kFwdKU = 4;
-constexpr int kBwdKU = 2;
+// Chunks per thread: two for the forward (four 16-byte loads) and two for the backward
+// (six). Measured against 1, 4 and 8 on R = 131072, H = 3072: within 1 %, except 8 for the
+// forward and 4 for the backward, 3-5 % slower.
+#ifndef MOE_SITU_FWD_KU
+#define MOE_SITU_FWD_KU 2
+#endif
+#ifndef MOE_SITU_BWD_KU
+#define MOE_SITU_BWD_KU 2
+#endif
+constexpr int kFwdKU = MOE_SITU_FWD_KU;
+constexpr int kBwdKU = MOE_SITU_BWD_KU;
 
 template <bool B4>
 __global__ __launch_bounds__(256) void situ_fwd_kernel(const uint16_t* __restrict__ h,
