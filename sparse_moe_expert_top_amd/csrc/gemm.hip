@@ -417,7 +417,6 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
                     lds_a + q * 1024);
         }
       }
-      if (kt + 1 < nk) fetch_a(kt + 1);
     };
     // B operand of stage kt: wave-uniform base and per-lane byte offsets (full stages), or
     // the per-lane source row (partial ragged-K stage; nullptr reads as zeros).
@@ -453,11 +452,21 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
                     lds_b + q * 1024);
         }
       }
-      if (kt + 1 < nk) fetch_b(kt + 1);
     };
     auto issue = [&](int kt) __attribute__((always_inline)) {
       issue_a(kt);
       issue_b(kt);
+    };
+    // Row indices of ragged-K stage kt (scalar loads, counted by lgkmcnt). Scalar loads may
+    // return out of order with LDS reads, so while one is pending every wait for fragments
+    // has to be lgkmcnt(0): the k-loop fetches stage kt's indices just before the wait that
+    // precedes its issue, where they land while the wave waits for the stage in flight
+    // (fetched right after an issue, they held up the next fragment wait by their latency).
+    auto fetch = [&](int kt) __attribute__((always_inline)) {
+      if (kt < nk) {
+        fetch_a(kt);
+        fetch_b(kt);
+      }
     };
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -530,11 +539,10 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
     //  * the reads of stage j+1 after all of its loads: each wavefront waits for its own
     //    loads of stage j+1 before the barrier that ends group 1's memory phase of stage j.
     static_assert(KS % 2 == 0, "fragment double buffer alternates within a stage");
+    static_assert(!(C::PP && KRAG), "the ping-pong k-loop serves fixed-K contractions");
     const int pgrp = C::PP ? (wave_u >> 2) : 0;
     auto kloop_pp = [&](auto nfc) __attribute__((always_inline)) {
       bf16x8 fa[2][FM], fb[2][FN];
-      fetch_a(0);
-      fetch_b(0);
 #pragma unroll
       for (int st = 0; st < 3; ++st)
         if (st < nk) issue(st);
@@ -560,28 +568,39 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
     };
     auto kloop_std = [&](auto nfc) __attribute__((always_inline)) {
       bf16x8 fa[2][FM], fb[2][FN];
-      fetch_a(0);
-      fetch_b(0);
 #pragma unroll
-      for (int st = 0; st < NS - 1; ++st)
+      for (int st = 0; st < NS - 1; ++st) {
+        fetch(st);
         if (st < nk) issue(st);
+      }
+      fetch(NS - 1);
       wait_stage(min(NS - 2, nk - 1));
       block_sync();
       if (NS - 1 < nk) issue(NS - 1);
       load_frags(nfc, 0, 0, fa[0], fb[0]);
-      for (int kt = 0; kt < nk; ++kt) {
-        const int slot = kt & (NS - 1);
+      // k-steps 0 .. KS-2 of the stage in `slot`; the last one's fragments end in fa[1]
+      auto first_steps = [&](int slot) __attribute__((always_inline)) {
 #pragma unroll
         for (int s = 0; s + 1 < KS; ++s) {
           load_frags(nfc, slot, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
           mfma_step(nfc, fa[s & 1], fb[s & 1]);
         }
-        if (kt + 1 < nk) {
-          wait_stage(min(NS - 2, nk - 2 - kt));
-          block_sync();
-          if (kt + NS < nk) issue(kt + NS);
-          load_frags(nfc, (kt + 1) & (NS - 1), 0, fa[0], fb[0]);
-        }
+      };
+      // The last stage is peeled off, so the last k-step's MFMAs of every other stage follow
+      // the next stage's first fragment reads on one path only: they use registers read
+      // before the barrier and wait for nothing (a join with the last stage's path made the
+      // compiler wait for those reads there).
+      for (int kt = 0; kt + 1 < nk; ++kt) {
+        first_steps(kt & (NS - 1));
+        fetch(kt + NS);
+        wait_stage(min(NS - 2, nk - 2 - kt));
+        block_sync();
+        if (kt + NS < nk) issue(kt + NS);
+        load_frags(nfc, (kt + 1) & (NS - 1), 0, fa[0], fb[0]);
+        mfma_step(nfc, fa[1], fb[1]);
+      }
+      if (nk > 0) {
+        first_steps((nk - 1) & (NS - 1));
         mfma_step(nfc, fa[1], fb[1]);
       }
       // every wave is done with the ring before the epilogue stages through it
