@@ -267,17 +267,22 @@ __global__ __launch_bounds__(512, 2) void w4a8_gemm_kernel(W4A8Args p) {
       if (NS - 1 < nk) issue(NS - 1);
       load_scales(nfc, 0, sa, sb);
       load_frags(nfc, 0, S0{}, fa0, fb0);
-      for (int kt = 0; kt < nk; ++kt) {
+      // the last stage is peeled off, so the last k-step's MFMAs of every other stage follow
+      // the next stage's first fragment reads on one path only and wait for nothing
+      for (int kt = 0; kt + 1 < nk; ++kt) {
         load_frags(nfc, kt % NS, S1{}, fa1, fb1);
         mfma_step(nfc, S0{}, fa0, fb0, sa, sb);
-        if (kt + 1 < nk) {
-          wait_stage(min(NS - 2, nk - 2 - kt));
-          block_sync();
-          if (kt + NS < nk) issue(kt + NS);
-          load_frags(nfc, (kt + 1) % NS, S0{}, fa0, fb0);
-        }
+        wait_stage(min(NS - 2, nk - 2 - kt));
+        block_sync();
+        if (kt + NS < nk) issue(kt + NS);
+        load_frags(nfc, (kt + 1) % NS, S0{}, fa0, fb0);
         mfma_step(nfc, S1{}, fa1, fb1, sa, sb);
-        if (kt + 1 < nk) load_scales(nfc, (kt + 1) % NS, sa, sb);
+        load_scales(nfc, (kt + 1) % NS, sa, sb);
+      }
+      if (nk > 0) {
+        load_frags(nfc, (nk - 1) % NS, S1{}, fa1, fb1);
+        mfma_step(nfc, S0{}, fa0, fb0, sa, sb);
+        mfma_step(nfc, S1{}, fa1, fb1, sa, sb);
       }
       wait_vm_lgkm0<0>();
       block_sync();
