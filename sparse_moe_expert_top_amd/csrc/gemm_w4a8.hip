@@ -26,8 +26,9 @@
 //    (32b + n). The instruction's sum of a block's products is not an fp32 round-to-nearest
 //    sum of the exact products: it deviated from one by up to 1.6e-4 of the sum of the
 //    products' magnitudes on full-range random codes and scales.
-//  * 256 x 256 tiles, 8 wavefronts (two per SIMD) of 64 x 128, K stages of 128 through an
-//    NS-slot LDS ring filled by direct-to-LDS loads: A [256][128 B] with chunk c of row r at
+//  * 256 x 256 tiles, 8 wavefronts (two per SIMD) of 64 x 128, K stages of 128 through a
+//    3-slot LDS ring (156 KiB: two stages in flight while one is read; 1-3 % faster than two
+//    slots) filled by direct-to-LDS loads: A [256][128 B] with chunk c of row r at
 //    c ^ ((r >> 1) & 7), B [256][64 B] with chunk c at c ^ ((r >> 2) & 3), so sixteen
 //    consecutive rows of one logical chunk hit sixteen distinct 16-byte slots; then each
 //    row's 4 scale bytes of the stage, A's and B's, one 4-byte load per row. Per stage and
@@ -71,7 +72,7 @@ struct W4A8Args {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 #ifndef MOE_W4_NS
-#define MOE_W4_NS 2
+#define MOE_W4_NS 3
 #endif
 
 template <int EPI>
