@@ -20,16 +20,16 @@
 // Scaled terms. The kernels work with E3 = 2 e3 (the exponential of 1 - 2|l| log2(e)/lambda
 // in base 2) and
 //   v1 = beta (1 - e1) / 2,  v3 = lambda (1 - e3) / 2,  q1 = (1 + e1) / 4,
-//   p2 = 1 + e2,  p3 = 1 + e3,  q12 = q1 p2,  r = 1 / (q12 p3) = 4 / ((1 + e1)(1 + e2)(1 + e3)),
-// each one fma, add, multiply or reciprocal. The powers of two are chosen so they cancel:
+//   q12 = q1 (1 + e2),  p3 = 1 + e3,  r = 1 / (q12 p3) = 4 / ((1 + e1)(1 + e2)(1 + e3)),
+// each one fma, multiply or reciprocal. The powers of two are chosen so they cancel:
 //   a = sgn(g) sgn(l) v1 sn v3 r                       (the 1/2, 1/2 and 4 cancel)
 //   dL/dl = da gate' 4 e3 / p3^2 = (sgn(g) v1 sn) E3 q12 (da r^2)
 //   dL/dg = da lin' d gate'/dg = (da r^2) (sgn(l) v3) N p3,
-//           N = e1 sn p2 / 2 + (sgn(g) v1) e2 q1
+//           N = e1 sn (1 + e2) / 2 + (sgn(g) v1) e2 q1
 // (d gate'/dg = (1 - tanh^2) sigmoid + beta tanh s (1 - s) over the common denominator
-// (1 + e1)^2 (1 + e2)^2, with 1/p3 = r q12 and 1/(q12^2 p3) = r^2 p3). Every p lies in [1, 2],
-// so r lies in [1/2, 4] and no intermediate overflows or underflows beyond the inputs' own
-// tails. Scaling by a power of two is exact, so a equals what the unscaled expressions give
+// (1 + e1)^2 (1 + e2)^2, with 1/p3 = r q12 and 1/(q12^2 p3) = r^2 p3). Every 1 + e lies in
+// [1, 2], so r lies in [1/2, 4] and no intermediate overflows or underflows beyond the inputs'
+// own tails. Scaling by a power of two is exact, so a equals what the unscaled expressions give
 // (barring fp32 denormals).
 // For tiny arguments 1 - e cancels, so beta (1 - exp(-y)) / 2 with y = 2|g|/beta is taken as
 // beta y / 2 = |g| when y < 2^-12 (relative error below y/2 < 2^-13, far under bf16's
@@ -78,7 +78,7 @@ __device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcp
 struct SituTerms {
   float e1, e2, E3;   // exp(-2|g|/beta), exp(-|g|), 2 exp(-2|l|/lambda)
   float v1, v3;       // >= 0
-  float q1, p2, p3, q12, r;
+  float q1, q12, p3, r;
 };
 
 template <bool B4>
@@ -91,9 +91,8 @@ __device__ __forceinline__ SituTerms situ_terms(float g, float l, const SituCoef
   t.v1 = (ag < c.t1) ? ag : fmaf(-c.hb, t.e1, c.hb);
   t.v3 = (al < c.t3) ? al : fmaf(-c.ql, t.E3, c.hl);
   t.q1 = fmaf(0.25f, t.e1, 0.25f);
-  t.p2 = 1.0f + t.e2;
+  t.q12 = fmaf(t.q1, t.e2, t.q1);
   t.p3 = fmaf(0.5f, t.E3, 1.0f);
-  t.q12 = t.q1 * t.p2;
   t.r = rcp_fast(t.q12 * t.p3);
   return t;
 }
