@@ -48,9 +48,10 @@ static int combine_cols(int64_t R_cap, int d, size_t avail) {
   return (int)(w / 256 * 256);
 }
 
-// Backward workspace: dh [R_cap, 2H] bf16 | dp partials [slots, R_cap] fp32 | overlay of
-// bf16(p a) [R_cap, H] and then the dX rows (fp32, one column window at a time).
-static size_t bwd_dh_bytes(int64_t R_cap, int H) { return round256((size_t)R_cap * 2 * H * 2); }
+// Backward workspace: dh [R_cap, 2H] bf16 (row stride dh_ld(H)) | dp partials [slots, R_cap]
+// fp32 | overlay of bf16(p a) [R_cap, H] and then the dX rows (fp32, one column window at a
+// time).
+static size_t bwd_dh_bytes(int64_t R_cap, int H) { return round256((size_t)R_cap * dh_ld(H) * 2); }
 static size_t bwd_dp_bytes(int64_t R_cap, int H) {
   return round256((size_t)gemm_da_slots(H) * (size_t)R_cap * 4);
 }

@@ -989,7 +989,7 @@ hipError_t launch_gemm_da(const uint16_t* dy, const int32_t* row_token, const in
   p.offsets = offsets; p.G = E_loc;
   p.N = H; p.K = d; p.H = H;
   p.n_tiles = (H + CDA::BN - 1) / CDA::BN;
-  p.o0 = dh; p.ld0 = 2 * H; p.o1 = pa; p.ld1 = H;
+  p.o0 = dh; p.ld0 = dh_ld(H); p.o1 = pa; p.ld1 = H;
   p.row_scale = row_gate; p.hsrc = h; p.dp_part = dp_part; p.dp_ld = R_cap;
   p.qsrc = h_codes; p.ssrc = h_scales;
   p.sc = c;
@@ -1004,7 +1004,7 @@ hipError_t launch_gemm_dx(const uint16_t* dh, const int32_t* offsets, int E_loc,
                           int64_t R_cap, int d, int H, int c0, int nc, const uint16_t* w_gu,
                           float* rows_out, hipStream_t s) {
   GemmArgs p = blank_args();
-  p.A = dh; p.lda = 2 * H;
+  p.A = dh; p.lda = dh_ld(H);
   p.B = w_gu + c0; p.ldb = d; p.b_gstride = (int64_t)2 * H * d;   // B(n, k) = w_gu[e][k][c0 + n]
   p.offsets = offsets; p.G = E_loc;
   p.N = nc; p.K = 2 * H;
@@ -1033,7 +1033,7 @@ hipError_t launch_gemm_dw_gu(const uint16_t* dh, const uint16_t* x, const int32_
                              const int32_t* offsets, int E_loc, int d, int H, float* dw_gu,
                              hipStream_t s) {
   GemmArgs p = blank_args();
-  p.A = dh; p.lda = 2 * H;                                    // A(m, k=r) = dh[r][m]
+  p.A = dh; p.lda = dh_ld(H);                                 // A(m, k=r) = dh[r][m]
   p.B = x; p.ldb = d; p.b_gather = row_token;                 // B(n, k=r) = x[tok(r)][n]
   p.group_m = MOE_GROUP_M_W;
   p.offsets = offsets; p.G = E_loc;
