@@ -14,7 +14,7 @@
 // branch: the lanes of the last block that run past the end rewrite the last chunk with the
 // same bytes its own lane writes. Launches are split by rows so each covers fewer than 2^32
 // chunks. No memory beyond the inputs and outputs is used, whatever R. Measured on MI355X at
-// R = 131072, H = 3072: 5.9-6.1 TB/s forward and 6.1-6.2 TB/s backward. A grid-stride walk
+// R = 131072, H = 3072: 5.8-6.2 TB/s forward and 6.1-6.2 TB/s backward. A grid-stride walk
 // of 256 workgroups per CU measured 3-6 % slower than one launch over every chunk, and plain
 // (temporal) loads 5-10 % slower.
 #include <hip/hip_runtime.h>
