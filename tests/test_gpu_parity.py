@@ -176,6 +176,43 @@ def test_situ_glu_extremes(moe):
     np.testing.assert_allclose(gdh, ref_dh, rtol=1e-2, atol=1e-6)
 
 
+@pytest.mark.parametrize("beta,linear_beta", [(3.0, 10.0), (1.0, 1.0), (7.5, 40.0)])
+def test_situ_glu_other_coefficients(moe, beta, linear_beta):
+    """beta != 4 takes the kernels' other path (exp(-|g|) evaluated on its own rather than as
+    the square of exp(-|g|/2)), and every coefficient enters the scaled terms: random rows and
+    the saturated and special inputs against the oracle at the same coefficients."""
+    say(f"situ_glu beta={beta} linear_beta={linear_beta}")
+    inp = situ_inputs(1000, 192, seed=5)
+    h, da = dev_bf16(inp["h"]), dev_bf16(inp["da"])
+    a = moe.situ_glu_fwd(h, beta=beta, linear_beta=linear_beta)
+    dh = moe.situ_glu_bwd(h, da, beta=beta, linear_beta=linear_beta)
+    torch.cuda.synchronize()
+    hf = oracle.bf16_widen(inp["h"])
+    ref_a = oracle.bf16_round(oracle.situ_glu_fwd(hf, 192, beta, linear_beta))
+    ref_dh = oracle.bf16_round(oracle.situ_glu_bwd(hf, oracle.bf16_widen(inp["da"]), 192, beta,
+                                                   linear_beta))
+    assert rel_err(host_bf16(a), ref_a) <= BF16_TOL
+    assert rel_err(host_bf16(dh), ref_dh) <= BF16_TOL
+    from moe_inputs import f32_to_bf16_bits
+    g = np.array([0.0, -0.0, 1e-30, -1e-30, 88.0, -88.0, 200.0, -200.0, 3e38, -3e38, 0.5, -1.2188,
+                  4.0, -4.0, 30.0, -30.0], np.float32)
+    l = np.array([0.0, 1.0, -1.0, 1e4, -1e4, 3e38, -3e38, 25.0, 0.5, -0.5, 100.0, 2.0, -60.0,
+                  60.0, 1e-20, 7.0], np.float32)
+    hb = f32_to_bf16_bits(np.concatenate([g.reshape(2, 8), l.reshape(2, 8)], axis=1))
+    db = f32_to_bf16_bits(np.ones((2, 8), np.float32))
+    a = moe.situ_glu_fwd(dev_bf16(hb), beta=beta, linear_beta=linear_beta)
+    dh = moe.situ_glu_bwd(dev_bf16(hb), dev_bf16(db), beta=beta, linear_beta=linear_beta)
+    torch.cuda.synchronize()
+    ga, gdh = host_bf16(a), host_bf16(dh)
+    assert np.all(np.isfinite(ga)) and np.all(np.isfinite(gdh))
+    hf = oracle.bf16_widen(hb)
+    np.testing.assert_allclose(ga, oracle.bf16_round(oracle.situ_glu_fwd(hf, 8, beta, linear_beta)),
+                               rtol=1e-2, atol=1e-35)
+    np.testing.assert_allclose(
+        gdh, oracle.bf16_round(oracle.situ_glu_bwd(hf, oracle.bf16_widen(db), 8, beta, linear_beta)),
+        rtol=1e-2, atol=1e-6)
+
+
 def test_situ_glu_full_size_sampled(moe):
     """h bf16 [131072, 6144] ~ N(0, 9), da [131072, 3072]: the streaming configuration; the
     oracle checks 4096 sampled rows."""
@@ -333,8 +370,10 @@ def compare_full(m, cfg, inp, R_cap=None, **buf_kw):
     idx, gates, perm = oracle_route_perm(inp, cfg)
     buf, t = run_layer(m, cfg, inp, R_cap, **buf_kw)
     check_route_perm(buf, idx, gates, perm)
-    f = oracle.expert_layer_fwd(inp["x"], inp["w_gu"], inp["w_down"], perm, cfg.H, mode="S")
+    f = oracle.expert_layer_fwd(inp["x"], inp["w_gu"], inp["w_down"], perm, cfg.H,
+                                beta=cfg.beta, linear_beta=cfg.linear_beta, mode="S")
     b = oracle.expert_layer_bwd(inp["x"], inp["dy"], inp["w_gu"], inp["w_down"], perm, cfg.H,
+                                beta=cfg.beta, linear_beta=cfg.linear_beta,
                                 mode="S")
     R = perm["R"]
     gy, gdx = host_bf16(buf.y), host_bf16(buf.dx)
@@ -370,6 +409,16 @@ def test_layer_full(moe, name):
         assert perm["R"] == 0
         assert not bool(buf.y.any()) and not bool(buf.dx.any()) and not bool(buf.dp.any())
         assert not bool(buf.dw_gu.any()) and not bool(buf.dw_down.any())
+
+
+def test_layer_other_coefficients(moe):
+    """beta = 2.5, linear_beta = 12: the gate/up epilogue's forward and the dA epilogue's
+    backward on the kernels' beta != 4 path, every output compared in full with the oracle at
+    the same coefficients."""
+    cfg = LayerConfig("mid_coef", T=2048, d=256, H=192, E=16, k=4, e_lo=2, E_loc=10, beta=2.5,
+                      linear_beta=12.0)
+    say(f"layer full {cfg.name}")
+    compare_full(moe, cfg, layer_inputs(cfg, seed=2))
 
 
 def random_layer_configs(n=32, seed=7):
@@ -516,8 +565,10 @@ def compare_sampled(m, cfg, n_tok=128, n_exp=4, n_col=14, seed=0, h_store="bf16"
                            rng.choice(cfg.T, 8, replace=False), [0, cfg.T - 1]])
     sub, rows = sub_perm(perm, toks)
     say(f"layer sampled {cfg.name}: oracle on {len(rows)} rows")
-    f = oracle.expert_layer_fwd(inp["x"], inp["w_gu"], inp["w_down"], sub, cfg.H, mode="S")
+    f = oracle.expert_layer_fwd(inp["x"], inp["w_gu"], inp["w_down"], sub, cfg.H,
+                                beta=cfg.beta, linear_beta=cfg.linear_beta, mode="S")
     b = oracle.expert_layer_bwd(inp["x"], inp["dy"], inp["w_gu"], inp["w_down"], sub, cfg.H,
+                                beta=cfg.beta, linear_beta=cfg.linear_beta,
                                 mode="S", h_store=h_store)
     toks = np.unique(toks)
     tt = torch.from_numpy(toks).cuda()
@@ -553,7 +604,8 @@ def compare_sampled(m, cfg, n_tok=128, n_exp=4, n_col=14, seed=0, h_store="bf16"
     for e in exps:
         say(f"layer sampled {cfg.name}: dW expert {e} rows {counts[e]}")
         gu, dn = oracle.dw_columns(inp["x"], inp["dy"], inp["w_gu"], inp["w_down"], perm, int(e),
-                                   cols, cfg.H, h_store=h_store)
+                                   cols, cfg.H, beta=cfg.beta, linear_beta=cfg.linear_beta,
+                                   h_store=h_store)
         ci = torch.from_numpy(np.concatenate([cols, cfg.H + cols])).cuda()
         got_gu_all.append(dwg[int(e)][ci].cpu().numpy())
         got_dn_all.append(dwd[int(e)][:, torch.from_numpy(cols).cuda()].cpu().numpy())
@@ -613,6 +665,7 @@ def test_router_bwd_end_to_end(moe, name):
     torch.cuda.synchronize()
     say(f"router bwd end to end {name}: oracle")
     b = oracle.expert_layer_bwd(inp["x"], inp["dy"], inp["w_gu"], inp["w_down"], perm, cfg.H,
+                                beta=cfg.beta, linear_beta=cfg.linear_beta,
                                 mode="S")
     ref = oracle.router_bwd(gates, b["dp"])
     errs = dict(dp=rel_err(buf.dp.cpu().numpy(), b["dp"]), dlogits=rel_err(dl.cpu().numpy(), ref))
@@ -673,7 +726,8 @@ def test_layer_mxfp8_store(moe, name):
     torch.cuda.synchronize()
     check_route_perm(buf, idx, gates, perm)
     R = perm["R"]
-    f = oracle.expert_layer_fwd(inp["x"], inp["w_gu"], inp["w_down"], perm, cfg.H, mode="S")
+    f = oracle.expert_layer_fwd(inp["x"], inp["w_gu"], inp["w_down"], perm, cfg.H,
+                                beta=cfg.beta, linear_beta=cfg.linear_beta, mode="S")
     assert np.array_equal(host_bf16(ref16.h[:R]), f["h"])          # h is exact on both sides
     ref_c, ref_s = oracle.mxfp8.quantize(f["h"])
     assert np.array_equal(buf.h_codes[:R].cpu().numpy(), ref_c)
@@ -681,6 +735,7 @@ def test_layer_mxfp8_store(moe, name):
     assert torch.equal(a_mx[:R].view(torch.int16), ref16.a[:R].view(torch.int16))
     assert torch.equal(buf.y.view(torch.int16), ref16.y.view(torch.int16))
     b = oracle.expert_layer_bwd(inp["x"], inp["dy"], inp["w_gu"], inp["w_down"], perm, cfg.H,
+                                beta=cfg.beta, linear_beta=cfg.linear_beta,
                                 mode="S", h_store="mxfp8")
     errs = dict(dx=rel_err(host_bf16(buf.dx), b["dx"]),
                 dw_gu=rel_err(buf.dw_gu.cpu().numpy(), b["dw_gu"]),
@@ -691,6 +746,7 @@ def test_layer_mxfp8_store(moe, name):
         assert v <= (FP32_TOL if k_ == "dp" else BF16_TOL), (k_, v)
     # the stored form matters: the oracle's bf16-store backward differs from the MXFP8 one
     b16 = oracle.expert_layer_bwd(inp["x"], inp["dy"], inp["w_gu"], inp["w_down"], perm, cfg.H,
+                                  beta=cfg.beta, linear_beta=cfg.linear_beta,
                                   mode="S")
     assert rel_err(b16["dp"], b["dp"]) > FP32_TOL
 
@@ -708,11 +764,13 @@ def test_layer_mxfp8_store_general(moe, name):
     check_route_perm(buf, idx, gates, perm)
     ref16, _ = run_layer(moe, cfg, inp)
     R = perm["R"]
-    f = oracle.expert_layer_fwd(inp["x"], inp["w_gu"], inp["w_down"], perm, cfg.H, mode="S")
+    f = oracle.expert_layer_fwd(inp["x"], inp["w_gu"], inp["w_down"], perm, cfg.H,
+                                beta=cfg.beta, linear_beta=cfg.linear_beta, mode="S")
     check_h_codes(buf.h_codes[:R].cpu().numpy(), buf.h_scales[:R].cpu().numpy(), f["h"], name)
     assert torch.equal(buf.a_fwd[:R].view(torch.int16), ref16.a_fwd[:R].view(torch.int16))
     assert torch.equal(buf.y.view(torch.int16), ref16.y.view(torch.int16))
     b = oracle.expert_layer_bwd(inp["x"], inp["dy"], inp["w_gu"], inp["w_down"], perm, cfg.H,
+                                beta=cfg.beta, linear_beta=cfg.linear_beta,
                                 mode="S", h_store="mxfp8")
     errs = dict(dx=rel_err(host_bf16(buf.dx), b["dx"]),
                 dw_gu=rel_err(buf.dw_gu.cpu().numpy(), b["dw_gu"]),
@@ -733,6 +791,9 @@ W4A8_CASES = {
     "w4a8_one_token": LayerConfig("w4a8_one_token", T=1, d=128, H=128, E=8, k=3, e_lo=0,
                                   E_loc=8),
     "w4a8_k_eq_E": LayerConfig("w4a8_k_eq_E", T=64, d=128, H=256, E=6, k=6, e_lo=0, E_loc=6),
+    # the SiTU-GLU epilogue on the kernels' beta != 4 path
+    "w4a8_coef": LayerConfig("w4a8_coef", T=512, d=256, H=128, E=8, k=2, e_lo=0, E_loc=8,
+                             beta=3.0, linear_beta=10.0),
 }
 
 

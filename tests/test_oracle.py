@@ -186,6 +186,28 @@ def test_situ_bwd_matches_autograd():
     np.testing.assert_allclose(situ_glu_fwd(h, H), out.detach().numpy(), rtol=1e-13, atol=1e-14)
 
 
+@pytest.mark.parametrize("beta,linear_beta", [(3.0, 10.0), (1.0, 1.0), (7.5, 40.0)])
+def test_situ_other_coefficients_match_autograd(beta, linear_beta):
+    """The coefficients are parameters of the op ("Frontier-scale RL with Kimi K3", section
+    "Streaming activations"): with beta != 4 and linear_beta != 25 the oracle's forward and
+    backward equal torch's fp64 composition of the same formula and its autograd."""
+    rng = np.random.default_rng(6)
+    H = 20
+    h = rng.standard_normal((30, 2 * H)) * 5.0
+    da = rng.standard_normal((30, H))
+    t = torch.tensor(h, requires_grad=True)
+    g, l = t.split(H, dim=-1)
+    out = torch.mul(torch.sigmoid(g) * torch.tanh(g / beta) * beta,
+                    torch.tanh(l / linear_beta) * linear_beta)
+    out.backward(torch.from_numpy(da))
+    np.testing.assert_allclose(situ_glu_fwd(h, H, beta, linear_beta), out.detach().numpy(),
+                               rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(situ_glu_bwd(h, da, H, beta, linear_beta), t.grad.numpy(),
+                               rtol=1e-12, atol=1e-14)
+    # and they differ from the default coefficients' results on these inputs
+    assert not np.allclose(situ_glu_fwd(h, H, beta, linear_beta), situ_glu_fwd(h, H))
+
+
 def test_naive_activation_saves_six_fp32_copies():
     """The pages say autograd keeps 6 fp32 copies of [R, H] for the naive activation and that
     the bf16 [R, 2H] input is 1/6 of that. Count autograd's saved storages."""
