@@ -363,6 +363,8 @@ SMALL_CASES = {
     "none_local": LayerConfig("none_local", T=128, d=128, H=64, E=64, k=2, e_lo=60, E_loc=4),
     "skew_tail_small": LayerConfig("skew_tail_small", T=512, d=128, H=64, E=64, k=4, e_lo=20,
                                    E_loc=8, bias="zipf"),
+    # the largest k: up to 32 local slots per token in the router, permute and both combines
+    "k32": LayerConfig("k32", T=200, d=128, H=64, E=48, k=32, e_lo=4, E_loc=40),
 }
 
 
