@@ -413,14 +413,17 @@ def test_layer_full(moe, name):
         assert not bool(buf.dw_gu.any()) and not bool(buf.dw_down.any())
 
 
+# mid's shape with coefficients other than beta = 4, linear_beta = 25
+COEF_CASE = LayerConfig("mid_coef", T=2048, d=256, H=192, E=16, k=4, e_lo=2, E_loc=10,
+                        beta=2.5, linear_beta=12.0)
+
+
 def test_layer_other_coefficients(moe):
     """beta = 2.5, linear_beta = 12: the gate/up epilogue's forward and the dA epilogue's
     backward on the kernels' beta != 4 path, every output compared in full with the oracle at
     the same coefficients."""
-    cfg = LayerConfig("mid_coef", T=2048, d=256, H=192, E=16, k=4, e_lo=2, E_loc=10, beta=2.5,
-                      linear_beta=12.0)
-    say(f"layer full {cfg.name}")
-    compare_full(moe, cfg, layer_inputs(cfg, seed=2))
+    say(f"layer full {COEF_CASE.name}")
+    compare_full(moe, COEF_CASE, layer_inputs(COEF_CASE, seed=2))
 
 
 def random_layer_configs(n=32, seed=7):
@@ -753,12 +756,13 @@ def test_layer_mxfp8_store(moe, name):
     assert rel_err(b16["dp"], b["dp"]) > FP32_TOL
 
 
-@pytest.mark.parametrize("name", ["tiny", "mid", "multi_tile"])
+@pytest.mark.parametrize("name", ["tiny", "mid", "multi_tile", "mid_coef"])
 def test_layer_mxfp8_store_general(moe, name):
     """The MXFP8-store layer on the workloads' own inputs (x ~ N(0,1), weights N(0, 1/fan_in)):
     the stored codes within the bound of check_h_codes; y, a and h's forward as in the
-    bf16-store path; dx, dW and dp against the oracle recomputing from its own stored h."""
-    cfg = SMALL_CASES[name]
+    bf16-store path; dx, dW and dp against the oracle recomputing from its own stored h.
+    mid_coef takes the MXFP8 epilogues' beta != 4 path."""
+    cfg = COEF_CASE if name == "mid_coef" else SMALL_CASES[name]
     say(f"layer mxfp8 general {name}")
     inp = layer_inputs(cfg, seed=0)
     idx, gates, perm = oracle_route_perm(inp, cfg)
