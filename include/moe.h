@@ -230,8 +230,9 @@ moe_status moe_grouped_gemm_down_combine_noalloc(const void* a, const int32_t* e
  *   dy, x [T, d] bf16; h [R_cap, 2H] bf16 (saved by the forward); metadata from
  *   moe_permute; dx [T, d] bf16 out; dw_gu [E_loc, 2H, d] fp32 out; dw_down [E_loc, d, H]
  *   fp32 out; dp [T, k] fp32 out.
- *   ws: dh [R_cap, 2H] bf16, the dp partials and an overlay of bf16(p a) [R_cap, H] with the
- *   fp32 dX rows. moe_workspace_size(MOE_WS_EXPERT_BWD, ...) bytes combine dx in one pass;
+ *   ws: dh [R_cap, 2H] bf16 (rows 2H + 64 elements apart), the dp partials and an overlay of
+ *   bf16(p a) [R_cap, H] with the fp32 dX rows. moe_workspace_size(MOE_WS_EXPERT_BWD, ...)
+ *   bytes combine dx in one pass;
  *   a smaller ws (down to moe_workspace_size_passes with passes = d / 256) runs the dX GEMM
  *   and its combine once per window of output columns (bit-identical results).
  *   dx is summed in fp32 over a token's slots and rounded to bf16 once.
