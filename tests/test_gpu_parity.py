@@ -551,11 +551,13 @@ def check_h_codes(got_c, got_s, h_ref, what):
     assert same_c >= 0.999 and same_s >= 0.999, (what, same_c, same_s)
 
 
-def compare_sampled(m, cfg, n_tok=128, n_exp=4, n_col=14, seed=0, h_store="bf16"):
+def compare_sampled(m, cfg, n_tok=128, n_exp=4, n_col=14, seed=0, h_store="bf16", repeats=0):
     """Sampled comparison at full size: tokens (all their local rows), their rows' h and a,
     and the weight-gradient columns of sampled experts (incl. empty ones). h_store="mxfp8"
     runs the MXFP8-store path; its stored codes are checked within a bound and its weight-
-    gradient columns are taken in whole 32-column blocks (a block shares one scale)."""
+    gradient columns are taken in whole 32-column blocks (a block shares one scale).
+    repeats > 0 runs that many more steps on the same inputs and requires every output
+    tensor to be bit-identical to the first step's."""
     mx = h_store == "mxfp8"
     say(f"layer sampled {cfg.name} ({h_store}): generating inputs")
     inp = layer_inputs(cfg, seed=0)
@@ -632,11 +634,25 @@ def compare_sampled(m, cfg, n_tok=128, n_exp=4, n_col=14, seed=0, h_store="bf16"
     if np.any(counts == 0):
         for e in np.nonzero(counts == 0)[0]:
             assert not bool(dwg[int(e)].any()) and not bool(dwd[int(e)].any())
+    if repeats:
+        first = {n_: getattr(buf, n_).clone() for n_ in ("y", "dx", "dp", "dw_gu", "dw_down")}
+        for i in range(repeats):
+            say(f"layer sampled {cfg.name}: repeat {i + 1} of {repeats}")
+            buf.step(t["x"], t["logits"], t["w_gu"], t["w_down"], t["dy"])
+            torch.cuda.synchronize()
+            for n_, v in first.items():
+                got = getattr(buf, n_)
+                if v.dtype == torch.bfloat16:
+                    got, v = got.view(torch.int16), v.view(torch.int16)
+                assert torch.equal(got, v), (cfg.name, "repeat", i + 1, n_)
 
 
 @pytest.mark.parametrize("name", ["shard", "skew", "skew_mid", "skew_tail", "large"])
 def test_layer_full_size_sampled(moe, name):
-    compare_sampled(moe, LAYER_CONFIGS[name])
+    """At shard and large, three more steps must reproduce every output bit for bit (the
+    persistent kernels' tile order, the scan-based permutation and the slot-order combines
+    are deterministic)."""
+    compare_sampled(moe, LAYER_CONFIGS[name], repeats=3 if name in ("shard", "large") else 0)
     torch.cuda.empty_cache()
 
 
