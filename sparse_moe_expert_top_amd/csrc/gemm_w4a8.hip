@@ -26,14 +26,19 @@
 //    (32b + n). The instruction's sum of a block's products is not an fp32 round-to-nearest
 //    sum of the exact products: it deviated from one by up to 1.6e-4 of the sum of the
 //    products' magnitudes on full-range random codes and scales.
-//  * 256 x 256 tiles, 8 wavefronts (two per SIMD) of 64 x 128, K stages of 128 through a
-//    3-slot LDS ring (156 KiB: two stages in flight while one is read; 1-3 % faster than two
-//    slots) filled by direct-to-LDS loads: A [256][128 B] with chunk c of row r at
-//    c ^ ((r >> 1) & 7), B [256][64 B] with chunk c at c ^ ((r >> 2) & 3), so sixteen
-//    consecutive rows of one logical chunk hit sixteen distinct 16-byte slots; then each
-//    row's 4 scale bytes of the stage, A's and B's, one 4-byte load per row. Per stage and
-//    wavefront: 4 A, 2 B and 1 scale load; per k-step and fragment two ds_read_b128 (A) or
-//    one (B), and one ds_read_b32 of the scales per stage.
+//  * 256 x 256 tiles, 8 wavefronts (two per SIMD) of 64 x 128, K stages of 128 filled by
+//    direct-to-LDS loads: A [256][128 B] with chunk c of row r at c ^ ((r >> 1) & 7),
+//    B [256][64 B] with chunk c at c ^ ((r >> 2) & 3), so sixteen consecutive rows of one
+//    logical chunk hit sixteen distinct 16-byte slots. Per stage and wavefront: 4 A and 2 B
+//    loads; per k-step and fragment two ds_read_b128 (A) or one (B), and one ds_read_b32 of
+//    the scales per stage.
+//  * Block scales. Each stage needs 4 scale bytes of each of the tile's 512 rows (A's and
+//    B's). When K is a multiple of 512 and at most 3584, a scale block beside a 2-slot ring
+//    (96 KiB + 56 KiB) holds them as 16-byte chunks of 4 stages, one 16-byte load per row and
+//    chunk, each chunk requested 4 stages before its first read. Otherwise a 3-slot ring
+//    (156 KiB) carries each stage's scale bytes in the stage slot, one 4-byte load per row and
+//    stage. Fetching a row's 4 bytes once per stage touches 512 cache lines per stage; the
+//    chunked block fetches each line a quarter as often.
 //  * The pipeline, tile list, balanced row split, XCD-aware order and fragment skipping are
 //    those of the bf16 grouped GEMM (gemm.hip, gemm_util.h).
 #include <hip/hip_runtime.h>
@@ -75,21 +80,32 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 #define MOE_W4_NS 3
 #endif
 
-template <int EPI>
+// SB selects where a stage's scale bytes come from. false: each stage slot of the ring holds
+// them, one 4-byte load per tile row and stage (512 rows: 512 cache lines per stage for 2 KiB).
+// true (K a multiple of 512 and at most 3584, scale arrays 16-byte aligned): a scale block
+// after a 2-slot ring holds all K / 128 stages of them for every tile row as 16-byte chunks
+// of 4 stages, [chunk][512 rows][16 bytes]; one 16-byte load per row fetches a chunk, so the
+// scale loads per tile drop from K / 128 to K / 512 per row. Chunk c + 1 is requested with
+// stage 4 c's refill, four stages before its first read.
+template <int EPI, bool SB>
 __global__ __launch_bounds__(512, 2) void w4a8_gemm_kernel(W4A8Args p) {
-  constexpr int BM = 256, BN = 256, BK = 128, NS = MOE_W4_NS, NT = 512, NW = 8;
+  constexpr int BM = 256, BN = 256, BK = 128, NS = SB ? 2 : MOE_W4_NS, NT = 512, NW = 8;
   constexpr int WGN = 2, WM = 64, WN = 128, FM = WM / 32, FN = WN / 32;
   constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK / 2, AS_BYTES = BM * 4, BS_BYTES = BN * 4;
-  constexpr int SC_OFF = A_BYTES + B_BYTES;        // A scales, then B scales
-  constexpr int STAGE = A_BYTES + B_BYTES + AS_BYTES + BS_BYTES;
+  constexpr int SC_OFF = A_BYTES + B_BYTES;        // A scales, then B scales (SB: unused)
+  constexpr int STAGE = A_BYTES + B_BYTES + (SB ? 0 : AS_BYTES + BS_BYTES);
+  constexpr int SB_CH = 7;                         // scale block: chunks of 4 stages (K <= 3584)
+  constexpr int SB_OFF = NS * STAGE;
+  constexpr int SB_BYTES = SB ? SB_CH * 512 * 16 : 0;
   constexpr int LA = A_BYTES / 1024 / NW;          // 16-byte direct loads per wave per stage
   constexpr int LB = B_BYTES / 1024 / NW;
-  constexpr int LPS = LA + LB + 1;                 // + one 4-byte scale load
+  constexpr int LPS = LA + LB + (SB ? 0 : 1);      // + one 4-byte scale load
   static_assert(LA == 4 && LB == 2 && AS_BYTES / 256 + BS_BYTES / 256 == NW, "stage loads");
   static_assert(NS == 2 || NS == 3, "ring depth");
+  static_assert(NW * 64 == 512, "scale block: one row per lane");
   constexpr bool GU = (EPI == W4_GATEUP);
 
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NS * STAGE + SB_BYTES];
   __shared__ int s_pref[1025];
   __shared__ int s_scan[NT];
 
@@ -112,6 +128,8 @@ __global__ __launch_bounds__(512, 2) void w4a8_gemm_kernel(W4A8Args p) {
   const uint32_t b_base = (uint32_t)(A_BYTES + (wn * WN + l32) * (BK / 2) + ((hh ^ ((l32 >> 2) & 3)) << 4));
   const uint32_t as_base = (uint32_t)(SC_OFF + (wm * WM + l32) * 4);
   const uint32_t bs_base = (uint32_t)(SC_OFF + AS_BYTES + (wn * WN + l32) * 4);
+  const uint32_t sb_as_base = (uint32_t)(SB_OFF + (wm * WM + l32) * 16);
+  const uint32_t sb_bs_base = (uint32_t)(SB_OFF + (256 + wn * WN + l32) * 16);
 
   const int nblk = gridDim.x;
   const int nk = p.K / BK;
@@ -155,6 +173,9 @@ __global__ __launch_bounds__(512, 2) void w4a8_gemm_kernel(W4A8Args p) {
     const uint8_t* a_tile = p.A + a_row0 * p.K;
     const uint8_t* as_tile = p.As + a_row0 * ks;
 
+    // waves 0..3 load the A scales of rows 64 w .. 64 w + 63, waves 4..7 the B scales
+    const bool s_is_a = wave_u < 4;
+    const uint8_t* s_src = s_is_a ? as_tile : Bsg;
     // ------------------------------------------------------------ load addressing
     uint32_t a_off[LA], b_off[LB], s_off;
 #pragma unroll
@@ -171,9 +192,6 @@ __global__ __launch_bounds__(512, 2) void w4a8_gemm_kernel(W4A8Args p) {
       const int c = ((byte & 63) >> 4) ^ ((row >> 2) & 3);
       b_off[q] = (uint32_t)w_row(row) * (uint32_t)(p.K / 2) + (uint32_t)(c << 4);
     }
-    // waves 0..3 load the A scales of rows 64 w .. 64 w + 63, waves 4..7 the B scales
-    const bool s_is_a = wave_u < 4;
-    const uint8_t* s_src = s_is_a ? as_tile : Bsg;
     s_off = (uint32_t)(s_is_a ? a_srow(wave * 64 + lane) : w_row((wave - 4) * 64 + lane)) *
             (uint32_t)ks;
 
@@ -181,7 +199,15 @@ __global__ __launch_bounds__(512, 2) void w4a8_gemm_kernel(W4A8Args p) {
       const uint32_t base = ring_lds + (kt % NS) * STAGE;
       dma_saddr<LA>(base + wave_u * (LA * 1024), uniform_ptr(a_tile + kt * BK), a_off);
       dma_saddr<LB>(base + A_BYTES + wave_u * (LB * 1024), uniform_ptr(Bg + kt * (BK / 2)), b_off);
-      dma_saddr_b32(base + SC_OFF + wave_u * 256, uniform_ptr(s_src + kt * 4), s_off);
+      if constexpr (!SB)
+        dma_saddr_b32(base + SC_OFF + wave_u * 256, uniform_ptr(s_src + kt * 4), s_off);
+    };
+    // SB: chunk c (the scale bytes of stages 4 c .. 4 c + 3) of the wavefront's 64 rows, 16
+    // bytes per lane, into [c][row]
+    auto issue_chunk = [&](int c) __attribute__((always_inline)) {
+      const uint32_t o1[1] = {s_off};
+      dma_saddr<1>(ring_lds + SB_OFF + c * (512 * 16) + wave_u * 1024,
+                   uniform_ptr(s_src + c * 16), o1);
     };
     auto wait_stage = [&](int later) __attribute__((always_inline)) {
       if (later >= 2) wait_vm_lgkm0<2 * LPS>();
@@ -221,17 +247,27 @@ __global__ __launch_bounds__(512, 2) void w4a8_gemm_kernel(W4A8Args p) {
     };
     // each lane's scale word of the stage holds blocks 0..3 of its row; shifted by 8 hh, its
     // byte 2 s is block 2 s + hh, the block of k-step s that this lane supplies
-    auto load_scales = [&](auto nfc, int slot, uint32_t (&sa)[FM], uint32_t (&sb)[FN])
+    // (SB: the word of stage kt in each fragment row's 112 bytes of the scale block)
+    auto load_scales = [&](auto nfc, int kt, uint32_t (&sa)[FM], uint32_t (&sb)[FN])
         __attribute__((always_inline)) {
       constexpr int NF = decltype(nfc)::value;
-      uint32_t ab = as_base + (uint32_t)(slot * STAGE), bb = bs_base + (uint32_t)(slot * STAGE);
+      constexpr int RS = SB ? 32 * 16 : 128;          // bytes from one fragment's rows to the next
+      uint32_t ab, bb;
+      if constexpr (SB) {
+        const uint32_t col = (uint32_t)(kt >> 2) * (512u * 16u) + (uint32_t)(kt & 3) * 4u;
+        ab = sb_as_base + col;
+        bb = sb_bs_base + col;
+      } else {
+        ab = as_base + (uint32_t)((kt % NS) * STAGE);
+        bb = bs_base + (uint32_t)((kt % NS) * STAGE);
+      }
       asm volatile("" : "+v"(ab));
       asm volatile("" : "+v"(bb));
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        if (i < NF) sa[i] = *(const uint32_t*)(ring + i * 128 + ab) >> (8 * hh);
+        if (i < NF) sa[i] = *(const uint32_t*)(ring + i * RS + ab) >> (8 * hh);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) sb[j] = *(const uint32_t*)(ring + j * 128 + bb) >> (8 * hh);
+      for (int j = 0; j < FN; ++j) sb[j] = *(const uint32_t*)(ring + j * RS + bb) >> (8 * hh);
     };
     auto mfma_step = [&](auto nfc, auto sc, const i32x8 (&af)[FM], const u32x4 (&bfr)[FN],
                          const uint32_t (&sa)[FM], const uint32_t (&sb)[FN])
@@ -260,6 +296,7 @@ __global__ __launch_bounds__(512, 2) void w4a8_gemm_kernel(W4A8Args p) {
       i32x8 fa0[FM], fa1[FM];
       u32x4 fb0[FN], fb1[FN];
       uint32_t sa[FM], sb[FN];
+      if constexpr (SB) issue_chunk(0);
 #pragma unroll
       for (int st = 0; st < NS - 1; ++st)
         if (st < nk) issue(st);
@@ -275,10 +312,12 @@ __global__ __launch_bounds__(512, 2) void w4a8_gemm_kernel(W4A8Args p) {
         mfma_step(nfc, S0{}, fa0, fb0, sa, sb);
         wait_stage(min(NS - 2, nk - 2 - kt));
         block_sync();
+        // (SB: chunk kt / 4 + 1 is waited for with stage kt + 2 and read from stage kt + 4)
+        if (SB && (kt & 3) == 0 && 4 * ((kt >> 2) + 1) < nk) issue_chunk((kt >> 2) + 1);
         if (kt + NS < nk) issue(kt + NS);
         load_frags(nfc, (kt + 1) % NS, S0{}, fa0, fb0);
         mfma_step(nfc, S1{}, fa1, fb1, sa, sb);
-        load_scales(nfc, (kt + 1) % NS, sa, sb);
+        load_scales(nfc, kt + 1, sa, sb);
       }
       if (nk > 0) {
         load_frags(nfc, (nk - 1) % NS, S1{}, fa1, fb1);
@@ -387,9 +426,9 @@ __global__ __launch_bounds__(512, 2) void w4a8_gemm_kernel(W4A8Args p) {
   }
 }
 
-template <int EPI>
-static hipError_t run_w4a8(const W4A8Args& args, int64_t max_tiles, hipStream_t s) {
-  auto kern = w4a8_gemm_kernel<EPI>;
+template <int EPI, bool SB>
+static hipError_t run_w4a8_kernel(const W4A8Args& args, int64_t max_tiles, hipStream_t s) {
+  auto kern = w4a8_gemm_kernel<EPI, SB>;
   static int occ = -1;
   if (occ < 0) {
     int o = 0;
@@ -401,6 +440,16 @@ static hipError_t run_w4a8(const W4A8Args& args, int64_t max_tiles, hipStream_t 
   if (grid < 1) return hipSuccess;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), 0, s, args);
   return hipGetLastError();
+}
+
+// The scale-block form needs 16-byte aligned scale rows (K a multiple of 512) and arrays, and
+// K <= 3584 (28 stages of scale bytes per row in LDS).
+template <int EPI>
+static hipError_t run_w4a8(const W4A8Args& args, int64_t max_tiles, hipStream_t s) {
+  const bool sb = args.K % 512 == 0 && args.K <= 3584 && (uintptr_t)args.As % 16 == 0 &&
+                  (uintptr_t)args.Bs % 16 == 0 && args.bs_gs % 16 == 0;
+  return sb ? run_w4a8_kernel<EPI, true>(args, max_tiles, s)
+            : run_w4a8_kernel<EPI, false>(args, max_tiles, s);
 }
 
 #ifndef MOE_GROUP_M

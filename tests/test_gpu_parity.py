@@ -816,6 +816,12 @@ W4A8_CASES = {
     # the SiTU-GLU epilogue on the kernels' beta != 4 path
     "w4a8_coef": LayerConfig("w4a8_coef", T=512, d=256, H=128, E=8, k=2, e_lo=0, E_loc=8,
                              beta=3.0, linear_beta=10.0),
+    # K a multiple of 512 (at most 3584): the kernels' per-tile scale block instead of
+    # per-stage scale loads; one 16-byte chunk of scales per row, and 7 (d = 3584, every
+    # chunk of a row) with 3 for down (H = 1536)
+    "w4a8_sb": LayerConfig("w4a8_sb", T=1024, d=512, H=512, E=8, k=2, e_lo=0, E_loc=8),
+    "w4a8_sb_deep": LayerConfig("w4a8_sb_deep", T=300, d=3584, H=1536, E=4, k=2, e_lo=0,
+                                E_loc=4),
 }
 
 
