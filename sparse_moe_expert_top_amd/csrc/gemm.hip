@@ -812,12 +812,12 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
               }
               auto hgv = [&](int i) __attribute__((always_inline)) {
                 if constexpr (HMX)
-                  return __builtin_amdgcn_ldexpf(e4m3_decode((qg[i >> 2] >> (8 * (i & 3))) & 0xFFu), xg);
+                  return __builtin_amdgcn_ldexpf(e4m3_code(qg[i >> 2], i & 3), xg);
                 else return (i & 1) ? bf16_hi(hg[i >> 1]) : bf16_lo(hg[i >> 1]);
               };
               auto hlv = [&](int i) __attribute__((always_inline)) {
                 if constexpr (HMX)
-                  return __builtin_amdgcn_ldexpf(e4m3_decode((ql[i >> 2] >> (8 * (i & 3))) & 0xFFu), xl);
+                  return __builtin_amdgcn_ldexpf(e4m3_code(ql[i >> 2], i & 3), xl);
                 else return (i & 1) ? bf16_hi(hl[i >> 1]) : bf16_lo(hl[i >> 1]);
               };
               u32x4 og, ol, oa;

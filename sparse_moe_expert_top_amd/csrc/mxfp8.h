@@ -33,12 +33,17 @@ __device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
   return (uint32_t)(X + 127);
 }
 
-// Value of an E4M3 code (the encoder never produces the NaN codes).
-__device__ __forceinline__ float e4m3_decode(uint32_t c) {
-  const uint32_t ex = (c >> 3) & 0xFu, m = c & 7u;
-  const float mag = ex ? __uint_as_float(((ex + 120u) << 23) | (m << 20))
-                       : (float)m * 0.001953125f;
-  return (c & 0x80u) ? -mag : mag;
+// Values of the E4M3 codes in bytes 2P and 2P + 1 of w, by gfx950's E4M3 -> fp32
+// conversion (v_cvt_pk_f32_fp8, OCP E4M3): exact for every finite code, subnormals and signed
+// zeros included (the encoder never produces the NaN codes).
+template <int P>
+__device__ __forceinline__ f32x2 e4m3_pair(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, P == 1);
+}
+// Value of code i (0..3) of w.
+__device__ __forceinline__ float e4m3_code(uint32_t w, int i) {
+  const f32x2 v = ((i >> 1) & 1) ? e4m3_pair<1>(w) : e4m3_pair<0>(w);
+  return v[i & 1];
 }
 
 // 8 consecutive elements of one block: codes packed little-endian into two words.
@@ -60,7 +65,7 @@ __device__ __forceinline__ void mx_decode8(u32x2 codes, uint32_t scale_byte, flo
   const int X = (int)scale_byte - 127;
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    v[i] = __builtin_amdgcn_ldexpf(e4m3_decode((codes[i >> 2] >> (8 * (i & 3))) & 0xFFu), X);
+    v[i] = __builtin_amdgcn_ldexpf(e4m3_code(codes[i >> 2], i & 3), X);
 }
 
 // Largest magnitude over the 4 lanes (xor 1, 2) that hold one 32-element block.
