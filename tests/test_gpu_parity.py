@@ -822,6 +822,8 @@ W4A8_CASES = {
     "w4a8_sb": LayerConfig("w4a8_sb", T=1024, d=512, H=512, E=8, k=2, e_lo=0, E_loc=8),
     "w4a8_sb_deep": LayerConfig("w4a8_sb_deep", T=300, d=3584, H=1536, E=4, k=2, e_lo=0,
                                 E_loc=4),
+    # K a multiple of 512 but above 3584 (32 stages): gate/up keeps the per-stage scale loads
+    "w4a8_k4096": LayerConfig("w4a8_k4096", T=256, d=4096, H=256, E=4, k=2, e_lo=0, E_loc=4),
 }
 
 
@@ -938,6 +940,39 @@ def test_w4a8_forward(moe, name):
     buf, perm = compare_w4a8_full(moe, cfg, inp)
     if name == "w4a8_none_local":
         assert perm["R"] == 0 and not bool(buf.y.any())
+
+
+def test_w4a8_scales_4_byte_aligned(moe):
+    """The C ABI lets the scale arrays be 4-byte aligned. The GEMMs then load each stage's
+    scale bytes per row instead of keeping the 16-byte-loaded scale block, with the same
+    products in the same order: gate/up's a codes and scales and down's y from 4-byte (not
+    16-byte) aligned copies of every scale array equal the aligned run's bit for bit (a shape
+    whose K suits the scale block, which test_w4a8_forward[w4a8_sb] compares with the
+    oracle)."""
+    cfg = W4A8_CASES["w4a8_sb"]
+    inp = layer_inputs(cfg, seed=5)
+    buf, w4 = run_w4a8(moe, cfg, inp)
+    R = buf.rows()
+    assert R > 0
+
+    def off4(t):
+        flat = torch.empty(t.numel() + 32, dtype=torch.uint8, device=t.device)
+        base = (-flat.data_ptr()) % 16 + 4
+        v = flat[base:base + t.numel()].view(t.shape)
+        v.copy_(t)
+        assert v.data_ptr() % 16 == 4
+        return v
+
+    a_c, a_s = moe.moe_grouped_gemm_gate_up_w4a8(
+        buf.x_codes, off4(buf.x_scales), buf.perm["row_token"], buf.perm["offsets"],
+        w4.gu_codes, off4(w4.gu_scales), buf.R_cap, cfg.beta, cfg.linear_beta)
+    y = moe.moe_grouped_gemm_down_combine_w4a8(
+        buf.a_codes, off4(buf.a_scales), buf.perm["offsets"], buf.perm["row_gate"],
+        buf.perm["slot_row"], w4.down_codes, off4(w4.down_scales), buf.R_cap)
+    torch.cuda.synchronize()
+    assert torch.equal(a_c[:R], buf.a_codes[:R])
+    assert torch.equal(a_s[:R], buf.a_scales[:R])
+    assert torch.equal(y.view(torch.int16), buf.y.view(torch.int16))
 
 
 def test_w4a8_exact_capacity(moe):
