@@ -357,6 +357,10 @@ moe_status moe_router_bwd(const float* gates, const float* dp, int64_t T, int k,
  * The products run on the block-scaled MFMA (fp32 accumulation; its per-block sums are not
  * round-to-nearest fp32 sums: results agree with an exact sum to about 2^-13 of the sum of
  * magnitudes at worst). d and H must be multiples of 128 (MOE_ERR_UNSUPPORTED otherwise).
+ * Speed, not results: a GEMM whose reduction length (d for gate/up, H for down) is a multiple
+ * of 512 and at most 3584, with both of its scale arrays 16-byte aligned, keeps its block
+ * scales in LDS for a whole tile; other shapes and 4-byte aligned scales load them per stage.
+ * Both forms give bit-identical results.
  */
 
 /*
