@@ -830,7 +830,9 @@ __global__ __launch_bounds__(C::NT, C::WPE) void grouped_gemm_kernel(GemmArgs p)
                   situ_bwd<B4>(hgv(2 * q), hlv(2 * q), pr * cv[2 * q], p.sc, a0, dg0, dl0);
                   situ_bwd<B4>(hgv(2 * q + 1), hlv(2 * q + 1), pr * cv[2 * q + 1], p.sc, a1, dg1,
                                dl1);
-                  const float ab0 = round_bf16(a0), ab1 = round_bf16(a1);
+                  // a0, a1 rounded to bf16 by one packed conversion (the same rounding)
+                  const uint32_t aw = pack_bf16x2(a0, a1);
+                  const float ab0 = bf16_lo(aw), ab1 = bf16_hi(aw);
                   acc_p = fmaf(cv[2 * q], ab0, acc_p);
                   acc_p = fmaf(cv[2 * q + 1], ab1, acc_p);
                   og[q] = pack_bf16x2(dg0, dg1);

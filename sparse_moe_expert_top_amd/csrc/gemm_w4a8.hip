@@ -247,7 +247,7 @@ __global__ __launch_bounds__(512, 2) void w4a8_gemm_kernel(W4A8Args p) {
     };
     // each lane's scale word of the stage holds blocks 0..3 of its row; shifted by 8 hh, its
     // byte 2 s is block 2 s + hh, the block of k-step s that this lane supplies
-    // (SB: the word of stage kt in each fragment row's 112 bytes of the scale block)
+    // (SB: the word of stage kt in chunk kt / 4 of each fragment row of the scale block)
     auto load_scales = [&](auto nfc, int kt, uint32_t (&sa)[FM], uint32_t (&sb)[FN])
         __attribute__((always_inline)) {
       constexpr int NF = decltype(nfc)::value;
