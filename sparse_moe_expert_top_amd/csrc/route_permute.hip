@@ -4,6 +4,8 @@
 // over the kept values). The dispatch metadata is the on-GPU form of the expert-sorted
 // token copy of "Kimi K3 ... Memory", section "MoE 反向" (second saving).
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 #include <math.h>
 
 #include "common.h"
@@ -288,6 +290,22 @@ __device__ __forceinline__ void load_token_routes(const int32_t* __restrict__ ro
 #pragma unroll
   for (int j = 0; j < KM; ++j) ev[j] = row[min(j, k - 1)];
 }
+// A token's KM route entries in 16-byte pieces (k == KM and 16-byte aligned rows).
+template <int KM, typename T>
+__device__ __forceinline__ void load_row_vec(const T* __restrict__ row, T (&v)[KM]) {
+  static_assert(sizeof(T) == 4 && KM % 4 == 0, "16-byte pieces of 4-byte entries");
+#pragma unroll
+  for (int q = 0; q < KM / 4; ++q) {
+    const u32x4 w = *(const u32x4*)(row + 4 * q);
+    // (element-wise conversions: a bit cast of one vector element reads element 0 on this
+    // compiler)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if constexpr (std::is_same<T, float>::value) v[4 * q + c] = __uint_as_float(w[c]);
+      else v[4 * q + c] = (T)w[c];
+    }
+  }
+}
 
 int permute_blocks(int64_t T) { return (int)((T + kPermTok - 1) / kPermTok); }
 
@@ -307,7 +325,8 @@ __global__ __launch_bounds__(256) void permute_count_kernel(const int32_t* __res
   const int64_t t = (int64_t)blockIdx.x * kPermTok + threadIdx.x;
   if (t < T) {
     int ev[KM];
-    load_token_routes(idx + t * k, k, ev);
+    if (k == KM && ((uintptr_t)idx & 15u) == 0) load_row_vec(idx + t * KM, ev);
+    else load_token_routes(idx + t * k, k, ev);
 #pragma unroll
     for (int j = 0; j < KM; ++j) {
       const int e = ev[j] - e_lo;
@@ -322,23 +341,35 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* cnt, int n,
                                                             int nblk, int E_loc, int64_t R_cap,
                                                             int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ status) {
-  __shared__ int part[1024];
+  __shared__ int wsum[16];
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
   const int seg = (n + 1023) / 1024;
   const int lo = tid * seg;
   const int hi = min(lo + seg, n);
   int local = 0;
   for (int i = lo; i < hi; ++i) local += cnt[i];
-  part[tid] = local;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over the 1024 partial sums
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int add = (tid >= off) ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += add;
-    __syncthreads();
+  // inclusive scan of the segment sums: within each wavefront by shuffles, then over the 16
+  // wavefront totals by the first wavefront
+  int x = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
   }
-  int run = part[tid] - local;        // exclusive prefix of this segment
+  if (lane == 63) wsum[wv] = x;
+  __syncthreads();
+  if (wv == 0) {
+    int t = (lane < 16) ? wsum[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      const int y = __shfl_up(t, off, 64);
+      if (lane >= off) t += y;
+    }
+    if (lane < 16) wsum[lane] = t;
+  }
+  __syncthreads();
+  int run = (wv ? wsum[wv - 1] : 0) + x - local;     // exclusive prefix of this segment
   for (int i = lo; i < hi; ++i) {
     const int c = cnt[i];
     cnt[i] = run;
@@ -346,7 +377,7 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* cnt, int n,
   }
   __threadfence_block();
   __syncthreads();
-  const int total = part[1023];
+  const int total = wsum[15];
   for (int e = tid; e < E_loc; e += 1024) {
     const int64_t b = (nblk > 0) ? cnt[(int64_t)e * nblk] : 0;
     offsets[e] = (int32_t)(b < R_cap ? b : R_cap);
@@ -364,6 +395,7 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
     int32_t* __restrict__ row_token, float* __restrict__ row_gate,
     int32_t* __restrict__ slot_row) {
   __shared__ uint32_t mask[1024 * 8];   // [expert][256 token bits]
+  __shared__ int first[1024 * 8];       // [expert][wave]: row of the wave's first route there
   for (int i = threadIdx.x; i < E_loc * 8; i += 256) mask[i] = 0;
   __syncthreads();
   const int tid = threadIdx.x;
@@ -371,9 +403,12 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
   const bool valid = t < T;
   const int w = tid >> 5;
   const uint32_t bit = 1u << (tid & 31);
+  // whole rows in 16-byte pieces when a token's k entries fill KM and the arrays allow it
+  const bool vec = k == KM && (((uintptr_t)idx | (uintptr_t)gates | (uintptr_t)slot_row) & 15u) == 0;
   int ev[KM];
   if (valid) {
-    load_token_routes(idx + t * k, k, ev);
+    if (vec) load_row_vec(idx + t * KM, ev);
+    else load_token_routes(idx + t * k, k, ev);
 #pragma unroll
     for (int j = 0; j < KM; ++j) {
       const int e = ev[j] - e_lo;
@@ -381,27 +416,50 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(
     }
   }
   __syncthreads();
+  // the block's first row of each expert plus the routes of the earlier wavefronts' tokens
+  for (int e = tid; e < E_loc; e += 256) {
+    int run = base[(int64_t)e * nblk + blockIdx.x];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      first[e * 8 + q] = run;
+      run += __popc(mask[e * 8 + q]);
+    }
+  }
+  __syncthreads();
   if (!valid) return;
   float gv[KM];
   const float* grow = gates + t * k;
+  if (vec) {
+    load_row_vec(grow, gv);
+  } else {
 #pragma unroll
-  for (int j = 0; j < KM; ++j) gv[j] = grow[min(j, k - 1)];
+    for (int j = 0; j < KM; ++j) gv[j] = grow[min(j, k - 1)];
+  }
+  int32_t srow[KM];
 #pragma unroll
   for (int j = 0; j < KM; ++j) {
+    srow[j] = -1;
     if (j >= k) continue;   // k is uniform; continue (not break) lets the loop unroll fully
     const int e = ev[j] - e_lo;
-    int32_t row = -1;
     if ((unsigned)e < (unsigned)E_loc) {
-      int rank = __popc(mask[e * 8 + w] & (bit - 1u));
-      for (int q = 0; q < w; ++q) rank += __popc(mask[e * 8 + q]);
-      const int64_t r = (int64_t)base[(int64_t)e * nblk + blockIdx.x] + rank;
+      const int64_t r = (int64_t)first[e * 8 + w] + __popc(mask[e * 8 + w] & (bit - 1u));
       if (r < R_cap) {
-        row = (int32_t)r;
+        srow[j] = (int32_t)r;
         row_token[r] = (int32_t)t;
         row_gate[r] = gv[j];
       }
     }
-    slot_row[t * k + j] = row;
+  }
+  if (vec) {
+#pragma unroll
+    for (int q = 0; q < KM / 4; ++q)
+      *(u32x4*)(slot_row + t * KM + 4 * q) =
+          u32x4{(uint32_t)srow[4 * q], (uint32_t)srow[4 * q + 1], (uint32_t)srow[4 * q + 2],
+                (uint32_t)srow[4 * q + 3]};
+  } else {
+#pragma unroll
+    for (int j = 0; j < KM; ++j)
+      if (j < k) slot_row[t * k + j] = srow[j];
   }
 }
 
