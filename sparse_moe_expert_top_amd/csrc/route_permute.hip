@@ -347,16 +347,8 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* cnt, int n,
   const int seg = (n + 1023) / 1024;
   const int lo = tid * seg;
   const int hi = min(lo + seg, n);
-  // the segment is read 16 entries at a time (clamped in-bounds indices, so the loads of a
-  // batch are issued together instead of one round trip per entry)
   int local = 0;
-  for (int b0 = lo; b0 < hi; b0 += 16) {
-    int v[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = cnt[min(b0 + j, hi - 1)];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) local += (b0 + j < hi) ? v[j] : 0;
-  }
+  for (int i = lo; i < hi; ++i) local += cnt[i];
   // inclusive scan of the segment sums: within each wavefront by shuffles, then over the 16
   // wavefront totals by the first wavefront
   int x = local;
@@ -378,17 +370,10 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(int32_t* cnt, int n,
   }
   __syncthreads();
   int run = (wv ? wsum[wv - 1] : 0) + x - local;     // exclusive prefix of this segment
-  for (int b0 = lo; b0 < hi; b0 += 16) {
-    int v[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = cnt[min(b0 + j, hi - 1)];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (b0 + j < hi) {
-        cnt[b0 + j] = run;
-        run += v[j];
-      }
-    }
+  for (int i = lo; i < hi; ++i) {
+    const int c = cnt[i];
+    cnt[i] = run;
+    run += c;
   }
   __threadfence_block();
   __syncthreads();
